@@ -1,0 +1,220 @@
+"""Pins of the fp64 CPU oracle against things other than itself.
+
+Every check here is independent of the oracle's own code path: a library
+routine (torch's casts, torch's scaled_dot_product_attention), a brute-force
+materialised computation written differently (log-sum-exp over a full masked
+matrix, math.fsum), closed forms, or invariants of causal softmax attention.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_bf16_causal_amd import synth
+
+
+def _decoded(inp):
+    """fp64 tensors of the inputs, decoded by torch's own casts (independent of
+    the oracle's decoders), times their dequantisation factors."""
+    dq, dk, dv = inp.descale
+    return (inp.q.to(torch.float64) * dq, inp.k.to(torch.float64) * dk, inp.v.to(torch.float64) * dv)
+
+
+def _oracle(inp, rows=None, nthreads=2):
+    dt = oracle.BF16 if inp.dtype == "bf16" else oracle.FP8_E4M3
+    dq, dk, dv = inp.descale
+    return oracle.attention(synth.raw_codes(inp.q), synth.raw_codes(inp.k), synth.raw_codes(inp.v), dt,
+                            inp.scale, dq, dk, dv, rows=rows, nthreads=nthreads)
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_e4m3fn_decoder_matches_torch_on_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.decode_e4m3fn(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+    assert np.nanmax(ours) == 448.0 and ours[0x7F] != ours[0x7F]  # 0x7F is NaN, 448 is the largest value
+
+
+def test_bf16_decoder_matches_torch_on_all_codes():
+    codes = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ours = oracle.dequantize(codes, oracle.BF16)
+    ref = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+# ---------------------------------------------------------------- brute force
+
+def _brute_force(qd, kd, vd, scale):
+    """Materialised causal attention via log-sum-exp over the full masked S x S
+    score matrix, with math.fsum; written independently of the oracle."""
+    B, S, Hq, _ = qd.shape
+    Hkv, Dv = kd.shape[2], vd.shape[3]
+    rep = Hq // Hkv
+    out = np.zeros((B, S, Hq, Dv))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // rep
+            scores = [[-math.inf] * S for _ in range(S)]
+            for i in range(S):
+                for j in range(S):
+                    if j <= i:
+                        scores[i][j] = scale * math.fsum(qd[b, i, h, d] * kd[b, j, g, d] for d in range(qd.shape[3]))
+            for i in range(S):
+                top = max(scores[i])
+                lse = top + math.log(math.fsum(math.exp(s - top) for s in scores[i] if s != -math.inf))
+                for d in range(Dv):
+                    out[b, i, h, d] = math.fsum(math.exp(scores[i][j] - lse) * vd[b, j, g, d] for j in range(i + 1))
+    return out
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("S,Hq,Hkv,D", [(1, 1, 1, 4), (7, 2, 1, 8), (13, 2, 2, 5), (16, 4, 2, 8)])
+def test_oracle_matches_brute_force(dtype, S, Hq, Hkv, D):
+    inp = synth.make_inputs(B=2, S=S, Hq=Hq, Hkv=Hkv, Dqk=D, Dv=D + 1, dtype=dtype, seed=S * 7 + Hq)
+    qd, kd, vd = (t.numpy() for t in _decoded(inp))
+    ref = _brute_force(qd, kd, vd, inp.scale)
+    got = _oracle(inp)
+    assert np.max(np.abs(got - ref)) <= 1e-13 * max(1.0, np.max(np.abs(ref)))
+
+
+# ---------------------------------------------------------------- library routine
+
+@pytest.mark.parametrize("dtype,B,S,Hq,Hkv,Dqk,Dv", [
+    ("bf16", 1, 200, 4, 4, 128, 128),
+    ("fp8", 2, 130, 4, 2, 128, 128),
+    ("fp8", 1, 97, 2, 1, 192, 128),
+    ("bf16", 1, 64, 3, 1, 64, 32),
+])
+def test_oracle_matches_torch_sdpa_float64(dtype, B, S, Hq, Hkv, Dqk, Dv):
+    inp = synth.make_inputs(B=B, S=S, Hq=Hq, Hkv=Hkv, Dqk=Dqk, Dv=Dv, dtype=dtype, seed=11 + S)
+    qd, kd, vd = _decoded(inp)
+    rep = Hq // Hkv
+    q = qd.permute(0, 2, 1, 3)
+    k = kd.repeat_interleave(rep, dim=2).permute(0, 2, 1, 3)
+    v = vd.repeat_interleave(rep, dim=2).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=inp.scale)
+    ref = ref.permute(0, 2, 1, 3).numpy()
+    got = _oracle(inp)
+    assert np.max(np.abs(got - ref)) <= 1e-12 * max(1.0, np.max(np.abs(ref)))
+
+
+def test_oracle_matches_sdpa_on_peaked_structure():
+    inp = synth.make_inputs(B=1, S=160, Hq=4, Hkv=1, Dqk=128, Dv=128, dtype="fp8", seed=2, structure="peaked")
+    qd, kd, vd = _decoded(inp)
+    q = qd.permute(0, 2, 1, 3)
+    k = kd.repeat_interleave(4, dim=2).permute(0, 2, 1, 3)
+    v = vd.repeat_interleave(4, dim=2).permute(0, 2, 1, 3)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=inp.scale)
+    got = _oracle(inp)
+    assert np.max(np.abs(got - ref.permute(0, 2, 1, 3).numpy())) <= 1e-11
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_row_zero_is_v0(dtype):
+    inp = synth.make_inputs(B=2, S=40, Hq=4, Hkv=2, Dqk=128, Dv=128, dtype=dtype, seed=3)
+    got = _oracle(inp)
+    _, _, vd = _decoded(inp)
+    for h in range(4):
+        assert np.array_equal(got[:, 0, h, :], vd[:, 0, h // 2, :].numpy())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_equal_scores_give_prefix_mean(dtype):
+    """scale = 0 makes every visible score equal: row i is the mean of V[0..i]."""
+    inp = synth.make_inputs(B=1, S=75, Hq=2, Hkv=1, Dqk=128, Dv=128, dtype=dtype, seed=4, scale=0.0)
+    got = _oracle(inp)
+    _, _, vd = _decoded(inp)
+    v = vd[0, :, 0, :].numpy()
+    prefix_mean = np.cumsum(v, axis=0) / np.arange(1, 76)[:, None]
+    for h in range(2):
+        assert np.max(np.abs(got[0, :, h, :] - prefix_mean)) <= 1e-13
+
+
+def test_zero_queries_give_prefix_mean():
+    inp = synth.make_inputs(B=1, S=33, Hq=1, Hkv=1, Dqk=128, Dv=64, dtype="bf16", seed=5)
+    inp.q.zero_()
+    got = _oracle(inp)
+    v = _decoded(inp)[2][0, :, 0, :].numpy()
+    assert np.max(np.abs(got[0, :, 0, :] - np.cumsum(v, axis=0) / np.arange(1, 34)[:, None])) <= 1e-13
+
+
+# ---------------------------------------------------------------- invariants
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_probability_rows_sum_to_one_and_are_causal(dtype):
+    inp = synth.make_inputs(B=1, S=24, Hq=2, Hkv=1, Dqk=16, Dv=16, dtype=dtype, seed=6)
+    dt = oracle.BF16 if dtype == "bf16" else oracle.FP8_E4M3
+    dq, dk, _ = inp.descale
+    P = oracle.probs(synth.raw_codes(inp.q), synth.raw_codes(inp.k), dt, inp.scale, 0, 1, dq, dk)
+    assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= 1e-14
+    lower = np.tril(np.ones_like(P, dtype=bool))
+    assert np.all(P[~lower] == 0.0) and np.all(P[lower] > 0.0)
+
+
+def test_score_shift_invariance():
+    """Adding one vector u to every key shifts each row's scores by a constant
+    (scale * q_i . u), which softmax ignores. Integer-valued BF16 inputs keep
+    K + u exact."""
+    g = torch.Generator().manual_seed(7)
+    B, S, H, D = 1, 50, 2, 16
+    q = torch.randint(-3, 4, (B, S, H, D), generator=g).to(torch.bfloat16)
+    k = torch.randint(-3, 4, (B, S, H, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, S, H, D), generator=g).to(torch.bfloat16)
+    u = torch.randint(-2, 3, (D,), generator=g).to(torch.bfloat16)
+    a = synth.AttnInputs(q, k, v, "bf16", 0.1, (1.0, 1.0, 1.0))
+    b = synth.AttnInputs(q, (k.float() + u.float()).to(torch.bfloat16), v, "bf16", 0.1, (1.0, 1.0, 1.0))
+    assert np.max(np.abs(_oracle(a) - _oracle(b))) <= 1e-12
+
+
+def test_gqa_equals_mha_with_repeated_kv():
+    inp = synth.make_inputs(B=2, S=70, Hq=6, Hkv=2, Dqk=32, Dv=48, dtype="fp8", seed=8)
+    rep = synth.AttnInputs(inp.q, inp.k.repeat_interleave(3, dim=2), inp.v.repeat_interleave(3, dim=2), "fp8",
+                           inp.scale, inp.descale)
+    assert np.array_equal(_oracle(inp), _oracle(rep))
+
+
+def test_v_column_permutation_permutes_output():
+    inp = synth.make_inputs(B=1, S=45, Hq=2, Hkv=2, Dqk=32, Dv=40, dtype="bf16", seed=9)
+    perm = torch.randperm(40, generator=torch.Generator().manual_seed(1))
+    per = synth.AttnInputs(inp.q, inp.k, inp.v[..., perm].contiguous(), "bf16", inp.scale, inp.descale)
+    assert np.array_equal(_oracle(inp)[..., perm.numpy()], _oracle(per))
+
+
+def test_descale_folding_and_output_linearity():
+    inp = synth.make_inputs(B=1, S=60, Hq=2, Hkv=1, Dqk=64, Dv=64, dtype="fp8", seed=10)
+    q, k, v = (synth.raw_codes(t) for t in (inp.q, inp.k, inp.v))
+    a = oracle.attention(q, k, v, oracle.FP8_E4M3, 0.2, dq=2.0, dk=0.5, dv=1.0)
+    b = oracle.attention(q, k, v, oracle.FP8_E4M3, 0.2, dq=1.0, dk=1.0, dv=1.0)
+    c = oracle.attention(q, k, v, oracle.FP8_E4M3, 0.2, dq=1.0, dk=1.0, dv=0.25)
+    assert np.max(np.abs(a - b)) <= 1e-14
+    assert np.array_equal(c, b * 0.25)
+
+
+def test_row_subset_matches_full():
+    inp = synth.make_inputs(B=2, S=90, Hq=4, Hkv=2, Dqk=128, Dv=128, dtype="fp8", seed=12)
+    full = _oracle(inp)
+    rows = np.array([[0, 0, 0], [1, 3, 89], [0, 2, 45], [1, 1, 1], [1, 0, 64]])
+    sub = _oracle(inp, rows=rows)
+    for n, (b, h, i) in enumerate(rows):
+        assert np.array_equal(sub[n], full[b, i, h])
+
+
+def test_oracle_rejects_bad_arguments():
+    inp = synth.make_inputs(B=1, S=8, Hq=3, Hkv=3, Dqk=8, Dv=8, dtype="bf16", seed=0)
+    q, k, v = (synth.raw_codes(t) for t in (inp.q, inp.k, inp.v))
+    with pytest.raises(ValueError):
+        oracle.attention(q, k, v, oracle.BF16, 1.0, rows=np.array([[0, 3, 0]]))  # head out of range
+    with pytest.raises(ValueError):
+        oracle.attention(q, k[:, :, :2], v[:, :, :2], oracle.BF16, 1.0)  # Hq % Hkv != 0
+    with pytest.raises(TypeError):
+        oracle.attention(q.astype(np.uint8), k, v, oracle.BF16, 1.0)
