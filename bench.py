@@ -1,0 +1,175 @@
+"""Benchmark: causal prefill attention TFLOP/s, FP8 and BF16, S=32K, head dim 128.
+
+One step is one pass of the whole path over one batch of seeded synthetic
+input: an FP8 e4m3 forward (B=1, H=32, S=32768, D=128, Gaussian, per-tensor
+scales) followed by a BF16 forward of the same shape, each one launch of the
+HIP library on torch's current stream, inputs already resident in HBM.
+
+FLOPs use the causal count B*H*S^2*(Dqk+Dv) (the visible half of the score
+matrix, two matrix products of 2 flop per multiply-add); the figure under the
+literal 2*B*H*S^2*(Dqk+Dv) formula is printed beside it. Peaks are MI355X's
+published dense matrix-core figures: 5.0 PFLOP/s FP8, 2.5 PFLOP/s BF16.
+
+Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "causal prefill attn TFLOP/s, FP8 & BF16, S=32K hd128; % of MFMA peak"
+PEAK = {"fp8": 5033.2, "bf16": 2516.6}  # TFLOP/s: 256 CU * 4 SIMD * {2048, 1024} flop/clk * 2.4 GHz
+PATHS = ["fp8_mha_s32k", "bf16_mha_s32k"]
+PAGES_TFLOPS = {"fp8_mha_s32k": 2672.0}  # the pages' own FP8 figure on this workload (context)
+
+
+def causal_flops(p):
+    return float(p["B"]) * p["Hq"] * p["S"] * p["S"] * (p["Dqk"] + p["Dv"])
+
+
+def read_sclk_mhz():
+    """Current shader clock from amd-smi (None when unavailable)."""
+    try:
+        r = subprocess.run(["amd-smi", "metric", "-g", "0", "--clock", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        data = json.loads(r.stdout)
+        d = data[0] if isinstance(data, list) else data
+        clk = d.get("clock", d)
+        for key in ("gfx_0", "GFX_0", "sclk", "gfx"):
+            if key in clk:
+                c = clk[key].get("clk", clk[key])
+                v = c.get("value") if isinstance(c, dict) else c
+                return float(v)
+    except Exception:
+        return None
+    return None
+
+
+def cpu_baseline(inputs, budget_rows, threads):
+    """The fp64 oracle, as it stands, on a bounded sample of rows of the same
+    workload, on the host cores."""
+    import numpy as np
+
+    import oracle
+    from fp8_bf16_causal_amd import synth
+
+    total_flop, total_s, parts = 0.0, 0.0, []
+    for name, inp in inputs.items():
+        p = inp.shape
+        rng = np.random.default_rng(2024)
+        n = budget_rows
+        rows = np.stack([np.zeros(n, dtype=np.int64), rng.integers(0, p["Hq"], n), rng.integers(0, p["S"], n)], 1)
+        q, k, v = synth.raw_codes(inp.q), synth.raw_codes(inp.k), synth.raw_codes(inp.v)
+        dt = oracle.BF16 if inp.dtype == "bf16" else oracle.FP8_E4M3
+        dq, dk, dv = inp.descale
+        t0 = time.perf_counter()
+        oracle.attention(q, k, v, dt, inp.scale, dq, dk, dv, rows=rows, nthreads=threads)
+        dt_s = time.perf_counter() - t0
+        flop = float(np.sum(rows[:, 2] + 1)) * 2.0 * (p["Dqk"] + p["Dv"])
+        total_flop += flop
+        total_s += dt_s
+        parts.append(f"{n} random (head, row) pairs of {name}")
+    return {"value": total_flop / total_s / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "; ".join(parts) + f"; {total_s:.1f} s of fp64 oracle time, causal flops of the sampled rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="rows per path in the CPU-baseline sample")
+    ap.add_argument("--paths", default=",".join(PATHS))
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import fp8_bf16_causal_amd as fbc
+    from fp8_bf16_causal_amd import synth
+
+    fbc._lib.load()
+    torch.cuda.set_device(0)
+    names = args.paths.split(",")
+    inputs = {n: synth.make_config(n, device="cuda") for n in names}
+    outs = {n: torch.empty((i.shape["B"], i.shape["S"], i.shape["Hq"], i.shape["Dv"]), dtype=torch.bfloat16,
+                           device="cuda") for n, i in inputs.items()}
+
+    def launch(n):
+        i = inputs[n]
+        dq, dk, dv = i.descale
+        fbc.flash_attn_func(i.q, i.k, i.v, i.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n])
+
+    for _ in range(args.warmup):
+        for n in names:
+            launch(n)
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each kernel bracketed by events on the launch stream
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+          for n in names}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for s in range(args.steps):
+        for n in names:
+            ev[n][s][0].record()
+            launch(n)
+            ev[n][s][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    sclk = read_sclk_mhz()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+
+    paths, flop_step, ideal_s = {}, 0.0, 0.0
+    for n in names:
+        p = inputs[n].shape
+        kind = inputs[n].dtype
+        ms = [a.elapsed_time(b) for a, b in ev[n]]
+        avg = sum(ms) / len(ms)
+        f = causal_flops(p)
+        flop_step += f
+        ideal_s += f / (PEAK[kind] * 1e12)
+        tf = f / (avg * 1e-3) / 1e12
+        paths[n] = {"kernel_ms_avg": round(avg, 4), "kernel_ms_min": round(min(ms), 4),
+                    "tflops": round(tf, 1), "tflops_literal_2x": round(2 * tf, 1),
+                    "peak_tflops": PEAK[kind], "frac_of_peak": round(tf / PEAK[kind], 4)}
+        if sclk:
+            paths[n]["frac_of_peak_at_measured_clock"] = round(tf / (PEAK[kind] * sclk / 2400.0), 4)
+        if n in PAGES_TFLOPS:
+            paths[n]["pages_tflops"] = PAGES_TFLOPS[n]
+            paths[n]["ratio_to_pages"] = round(tf / PAGES_TFLOPS[n], 3)
+
+    value = flop_step / (ms_per_step * 1e-3) / 1e12
+    dom = max(names, key=lambda n: paths[n]["kernel_ms_avg"])
+    dom_kind = inputs[dom].dtype
+    roofline = {"bound": "mfma", "achieved": paths[dom]["tflops"], "peak": PEAK[dom_kind], "unit": "TFLOP/s",
+                "frac": paths[dom]["frac_of_peak"], "traffic": None, "kernel": dom}
+    cfg = {"workload": "+".join(names), "B": 1, "H": 32, "S": 32768, "Dqk": 128, "Dv": 128,
+           "input": "Gaussian N(0,1), seeds 3 (fp8) and 4 (bf16), per-tensor e4m3 scales",
+           "flop_count": "causal B*H*S^2*(Dqk+Dv)"}
+    line = {"metric": METRIC, "value": round(value, 1), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "+".join(sorted({inputs[n].dtype for n in names})), "data": "synthetic",
+            "config": cfg, "frac_of_peak": round(ideal_s / (ms_per_step * 1e-3), 4),
+            "sclk_mhz_after_timing": sclk, "paths": paths, "roofline": roofline}
+    if not args.no_cpu_baseline:
+        threads = min(int(os.environ.get("OMP_NUM_THREADS", "16")), os.cpu_count() or 1, 16)
+        line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_rows, threads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,2 +1,70 @@
-"""MI355X (gfx950) causal prefill attention forward, FP8 e4m3 and BF16 inputs, BF16 output."""
+"""MI355X (gfx950) causal prefill attention forward: FP8 e4m3 or BF16 inputs,
+BF16 output, through the C-ABI library libfp8_bf16_causal.so.
+
+``attn_fwd`` / ``attn_fwd_ex`` / ``attn_strerror`` are the C entry points
+(device addresses as ints); ``flash_attn_func`` takes torch tensors. PyTorch
+only provides device memory and the stream.
+"""
+from __future__ import annotations
+
+import math
+
 from . import synth  # noqa: F401
+from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FP8_E4M3, ATTN_OK,
+                   attn_fwd, attn_fwd_ex, attn_strerror)
+
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_strerror", "flash_attn_func", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
+           "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH"]
+
+
+def _raise(code: int):
+    msg = attn_strerror(code)
+    if code == ATTN_ERR_INVALID:
+        raise ValueError(msg)
+    if code == ATTN_ERR_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, descale_k=None, descale_v=None,
+                    out=None):
+    """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
+    layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
+    factors. Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
+    enqueued on the current stream."""
+    import torch
+
+    if q.dtype == torch.bfloat16:
+        dtype = ATTN_BF16
+    elif q.dtype == torch.float8_e4m3fn:
+        dtype = ATTN_FP8_E4M3
+    else:
+        raise TypeError(f"q must be bfloat16 or float8_e4m3fn, got {q.dtype}")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k and v must have the same dtype")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [batch, seq, heads, dim]")
+    if not (q.is_cuda and k.is_cuda and v.is_cuda and q.device == k.device == v.device):
+        raise ValueError("q, k, v must be on one GPU")
+    if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
+        raise ValueError("q, k, v must be contiguous")
+    B, S, Hq, Dqk = q.shape
+    if k.shape[:2] != (B, S) or v.shape[:3] != k.shape[:3] or k.shape[3] != Dqk:
+        raise ValueError("shape mismatch between q, k and v")
+    Hkv, Dv = k.shape[2], v.shape[3]
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(Dqk)
+    if out is None:
+        out = torch.empty((B, S, Hq, Dv), dtype=torch.bfloat16, device=q.device)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != (B, S, Hq, Dv) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 [B, S, Hq, Dv] tensor")
+    ds = None
+    if dtype == ATTN_FP8_E4M3 and any(x is not None for x in (descale_q, descale_k, descale_v)):
+        ds = tuple(1.0 if x is None else float(x) for x in (descale_q, descale_k, descale_v))
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    with torch.cuda.device(q.device):
+        rc = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, Dqk, Dv,
+                         1 if causal else 0, float(softmax_scale), dtype, ds, stream, 0)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return out

@@ -1,0 +1,57 @@
+"""ctypes binding of libfp8_bf16_causal.so: the C entry points under the same
+names, with argument marshalling only (every step of the computation runs in
+the library's HIP kernels)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+ATTN_BF16 = 0
+ATTN_FP8_E4M3 = 1
+ATTN_OK = 0
+ATTN_ERR_INVALID = -1
+ATTN_ERR_UNSUPPORTED = -2
+ATTN_ERR_LAUNCH = -3
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8_bf16_causal.so")
+_lib = None
+
+
+def load():
+    """Load the built library; raises if it has not been built (there is no
+    fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; "
+                           "g.build()' or python -m fp8_bf16_causal_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, f32, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32]
+    lib.attn_fwd.restype = i32
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                ctypes.POINTER(ctypes.c_float), vp, u32]
+    lib.attn_fwd_ex.restype = i32
+    lib.attn_strerror.argtypes = [i32]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def attn_fwd(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype) -> int:
+    """q, k, v, out: device addresses (ints). Returns the library's code."""
+    return load().attn_fwd(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype)
+
+
+def attn_fwd_ex(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv=None, stream=None,
+                flags=0) -> int:
+    """descale_qkv: (dq, dk, dv) or None; stream: a hipStream_t as int, or None."""
+    ds = None
+    if descale_qkv is not None:
+        ds = (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
+    return load().attn_fwd_ex(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, ds, stream, flags)
+
+
+def attn_strerror(code: int) -> str:
+    return load().attn_strerror(code).decode()

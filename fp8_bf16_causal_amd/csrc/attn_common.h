@@ -1,0 +1,131 @@
+// attn_common.h -- shared pieces of the gfx950 causal prefill attention kernels:
+// vector types, matrix-core and cross-lane wrappers, LDS helpers, the launch
+// parameter block and the workgroup -> (batch, head, query block) mapping.
+//
+// Register layouts used throughout (gfx950, wave64; measured on the device):
+//  * v_mfma_f32_32x32x16_bf16: A lane (i = l%32, g = l/32) holds A[i][8g .. 8g+7],
+//    B lane (j, g) holds B[8g .. 8g+7][j]; D lane (j = l%32, g) register r holds
+//    D[8(r/4) + 4g + r%4][j].
+//  * v_mfma_scale_f32_32x32x64_f8f6f4: a lane's bytes 0-15 are K-half 0 and
+//    bytes 16-31 K-half 1 (byte b of A lane (i, g) pairs with byte b of B lane
+//    (j, g)); the E8M0 scale of (row or column i, K-half kb) is the byte taken
+//    from lane i + 32*kb. D layout as for the 32x32 bf16 instruction.
+//  * v_mfma_scale_f32_16x16x128_f8f6f4: lane (i = l%16, g = l/16) bytes 0-15
+//    cover K in [0, 64), bytes 16-31 cover K in [64, 128); the scale of
+//    (i, 32-wide K block kb) comes from lane i + 16*kb. D lane (j = l%16, g)
+//    register r holds D[4g + r][j].
+//  * ds_read_b64_tr_b8: within each 16-lane group, lanes 2b and 2b+1 supply
+//    the addresses of the two 8-byte halves of "row" b (b = 0..7); lane c
+//    receives byte c of each of the 8 rows.
+//  * ds_read_b64_tr_b16: within each 16-lane group, lanes 4b..4b+3 supply the
+//    four 8-byte quarters of row b (b = 0..3); lane c receives element c of
+//    each of the 4 rows.
+//  * v_permlane32_swap(x, y): x' = [x.lo32, y.lo32], y' = [x.hi32, y.hi32].
+//  * v_permlane16_swap(x, y) on 16-lane rows R0..R3:
+//    x' = [x.R0, y.R0, x.R2, y.R2], y' = [x.R1, y.R1, x.R3, y.R3].
+//  * v_cvt_pk_u8_f32 rounds half to even and saturates to [0, 255]; -inf and
+//    NaN give 0.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fbc {
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// Work decomposition: 8 waves per workgroup (two per SIMD), 32 query rows
+// per wave, 256 query rows per workgroup.
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kQW = 32;
+constexpr int kBQ = kWaves * kQW;
+constexpr int kXcds = 8;      // MI355X: 8 accelerator complex dies, each with its own L2
+constexpr int kOStride = 272; // epilogue staging: bytes per 128-wide BF16 output row in LDS
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  int B, Hq, Hkv, S;
+  int G;          // Hq / Hkv
+  int nqb;        // query blocks per head, ceil(S / kBQ)
+  int xcd_group;  // 1: every KV head's workgroups run on one XCD
+  float c;        // softmax scale * dq * dk * log2(e) (> 0)
+  float dv;       // output dequantisation factor
+};
+
+// Workgroup -> (batch, query head, query block). Heaviest (latest) query blocks
+// first, so the causal tail finishes on light work. Workgroups are dispatched
+// to XCDs round-robin (bid % 8); when the KV heads split evenly over the XCDs,
+// each XCD takes whole KV heads and walks them one at a time, so the
+// workgroups resident on an XCD stream the same K/V tiles through its L2.
+__device__ inline void map_block(const AttnParams& p, int bid, int& b, int& h, int& qb) {
+  const int per_head = p.G * p.nqb;
+  int kvh, s;
+  if (p.xcd_group) {
+    const int x = bid % kXcds, slot = bid / kXcds;
+    kvh = x + kXcds * (slot / per_head);
+    s = slot % per_head;
+    qb = p.nqb - 1 - s / p.G;
+  } else {
+    const int nkv = p.B * p.Hkv;
+    qb = p.nqb - 1 - bid / (nkv * p.G);
+    s = bid % (nkv * p.G);
+    kvh = s / p.G;
+  }
+  const int gi = s % p.G;
+  b = kvh / p.Hkv;
+  h = (kvh % p.Hkv) * p.G + gi;
+}
+
+__device__ inline v16f mfma_32x32x64_fp8(v8i a, v8i b, v16f c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+__device__ inline v4f mfma_16x16x128_fp8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
+}
+__device__ inline v16f mfma_32x32x16_bf16(v8bf a, v8bf b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ inline uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// max over the two 32-lane halves: every lane gets max(x[l], x[l ^ 32])
+__device__ inline float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+  return fmaxf(as_f(r[0]), as_f(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
+  return as_f(r[0]) + as_f(r[1]);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ inline v2i lds_read_tr8(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(lds_u8*)p);
+}
+__device__ inline v4s lds_read_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s*)(lds_u8*)p);
+}
+
+__device__ inline v4i ld_global16(const uint8_t* p) { return *(const v4i*)p; }
+__device__ inline v4i ld_lds16(const uint8_t* p) { return *(const v4i*)p; }
+__device__ inline void st_lds16(uint8_t* p, v4i x) { *(v4i*)p = x; }
+
+__device__ inline uint32_t pack_bf16(float lo, float hi) {
+  v2bf v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+}  // namespace fbc

@@ -1,0 +1,16 @@
+// attn_launch.h -- internal launchers of the attention kernels (not part of
+// the public ABI; see include/fp8_bf16_causal.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fbc {
+
+struct AttnParams;
+
+// One workgroup of 512 threads per (batch, query head, 256-row query block);
+// grid = B * Hq * ceil(S / 256). dqk is 128 or 192 (Dv is 128).
+hipError_t launch_attn_fwd_fp8(const AttnParams& p, int dqk, int grid, hipStream_t stream);
+hipError_t launch_attn_fwd_bf16(const AttnParams& p, int dqk, int grid, hipStream_t stream);
+
+}  // namespace fbc

@@ -1,0 +1,106 @@
+/*
+ * fp8_bf16_causal.h -- C ABI of the MI355X (gfx950) causal prefill attention
+ * forward library, libfp8_bf16_causal.so.
+ *
+ * The operation: causal prefill FlashAttention forward,
+ *   out = softmax(Q K^T * scale + causal mask) V,
+ * with BF16 or FP8 e4m3 inputs and BF16 output, for one MI355X.
+ *   [ZYFA abstract, "ZYFA: Speed and Accuracy of FP8 FlashAttention on AMD
+ *    CDNA4" (airebao.com page): prefill kernels for the MI355X, FlashAttention
+ *    with the softmax between the two matrix products;
+ *    spbcomputers.ru ZYFA article, opening paragraphs and FAQ: causal forward
+ *    only, FP8 e4m3 and BF16, an interface compatible with flash_attn_func,
+ *    no decode and no paged KV.]
+ *
+ * Conventions (flash_attn_func's public ones, where the pages give none):
+ *   - layout (batch, seq, heads, dim), contiguous:
+ *       q   [B][S][Hq][Dqk]
+ *       k   [B][S][Hkv][Dqk]
+ *       v   [B][S][Hkv][Dv]
+ *       out [B][S][Hq][Dv]   always BF16
+ *   - grouped-query attention: query head h reads KV head h / (Hq / Hkv);
+ *   - queries and keys have the same length S; key j is visible to query i
+ *     iff j <= i;
+ *   - FP8 inputs are OCP e4m3fn codes (torch.float8_e4m3fn) with one
+ *     dequantisation factor per tensor: the score scale is scale*dq*dk and dv
+ *     multiplies the output.
+ *
+ * FP8 softmax: each probability's e4m3 code is written directly from its
+ * score with one multiply-add and one integer convert (the code of 2^x is
+ * about 8x plus a constant); each 64-key block of a row is scaled by a power
+ * of two before rounding and the scaled matrix instruction removes the factor;
+ * the output is divided by the sum of the already-rounded probabilities.
+ *   [spbcomputers.ru ZYFA article, section "Три приёма, которые дали
+ *    ускорение"; captivela.com "Zyphra Luncurkan ZYFA", section "Tiga Trik
+ *    ZYFA Biar Cepat dan Akurat"; ZYFA abstract, techniques (1) and (3).]
+ *
+ * Memory and threading: every pointer is device memory owned by the caller.
+ * The library allocates nothing, keeps no pointer after returning and needs
+ * no workspace. Calls are asynchronous: they return once the kernel is
+ * enqueued on the stream; out is valid after the stream synchronises. Calls
+ * on different streams are independent; the library holds no mutable state.
+ *
+ * Errors: every entry point returns an int; nothing else crosses the ABI.
+ * Arguments are checked on the host before anything is enqueued; on an error
+ * return nothing was launched and out is untouched.
+ */
+#ifndef FP8_BF16_CAUSAL_H
+#define FP8_BF16_CAUSAL_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k and v. out is always BF16. */
+enum { ATTN_BF16 = 0, ATTN_FP8_E4M3 = 1 };
+
+/* Return codes. */
+enum {
+  ATTN_OK = 0,
+  /* a null or misaligned pointer (q, k, v, out must be 16-byte aligned), a
+   * size <= 0, Hq not a multiple of Hkv, scale negative or not finite, a
+   * descale factor <= 0 or not finite, a non-zero flags word, or sizes whose
+   * products (tensor bytes, workgroup count) overflow the index types */
+  ATTN_ERR_INVALID = -1,
+  /* causal == 0 (the method is causal-only), an unknown dtype, a head-dim
+   * pair other than (Dqk, Dv) = (128, 128) or (192, 128), or a current device
+   * that is not gfx950 */
+  ATTN_ERR_UNSUPPORTED = -2,
+  /* the HIP runtime reported an error when querying the device or launching */
+  ATTN_ERR_LAUNCH = -3
+};
+
+/*
+ * attn_fwd: causal prefill attention forward on the current device's null
+ * stream, with all dequantisation factors equal to 1.
+ *
+ *   q, k, v  device pointers to the inputs, dtype elements, layout above
+ *   out      device pointer to B*S*Hq*Dv BF16 values (written entirely)
+ *   B, Hq, Hkv, S, Dqk, Dv   sizes; Hq % Hkv == 0
+ *   causal   must be 1
+ *   scale    softmax scale (flash_attn_func's default is 1/sqrt(Dqk)), >= 0
+ *   dtype    ATTN_BF16 or ATTN_FP8_E4M3
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S, int Dqk,
+             int Dv, int causal, float scale, int dtype);
+
+/*
+ * attn_fwd_ex: attn_fwd with per-tensor dequantisation factors and a stream.
+ *
+ *   descale_qkv  host pointer to {dq, dk, dv}, or NULL for {1, 1, 1}; read
+ *                during the call only
+ *   stream       a hipStream_t, or NULL for the null stream
+ *   flags        reserved, must be 0
+ */
+int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S, int Dqk,
+                int Dv, int causal, float scale, int dtype, const float* descale_qkv, void* stream,
+                unsigned flags);
+
+/* A static, human-readable description of a return code (never NULL). */
+const char* attn_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8_BF16_CAUSAL_H */

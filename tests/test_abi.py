@@ -1,0 +1,81 @@
+"""The C-ABI library loads, exports what include/*.h declares, and rejects
+malformed arguments on the host (these paths return before any HIP call)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import fp8_bf16_causal_amd as fbc
+from fp8_bf16_causal_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    declared = _declared_functions()
+    assert {"attn_fwd", "attn_fwd_ex", "attn_strerror"} <= set(declared)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_codes():
+    for code in (fbc.ATTN_OK, fbc.ATTN_ERR_INVALID, fbc.ATTN_ERR_UNSUPPORTED, fbc.ATTN_ERR_LAUNCH, 12345):
+        assert isinstance(fbc.attn_strerror(code), str) and fbc.attn_strerror(code)
+    assert fbc.attn_strerror(fbc.ATTN_OK) != fbc.attn_strerror(fbc.ATTN_ERR_INVALID)
+
+
+# A fake, 16-byte aligned, never dereferenced address: every call below must be
+# rejected before the library touches the device.
+P = 1 << 20
+GOOD = dict(B=1, Hq=4, Hkv=2, S=128, Dqk=128, Dv=128, causal=1, scale=0.088, dtype=fbc.ATTN_BF16)
+
+
+def _call(ptrs=(P, P, P, P), descale=None, flags=0, **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fbc.attn_fwd_ex(*ptrs, a["B"], a["Hq"], a["Hkv"], a["S"], a["Dqk"], a["Dv"], a["causal"], a["scale"],
+                           a["dtype"], descale, None, flags)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(ptrs=(0, P, P, P)), dict(ptrs=(P, P, P, 0)), dict(ptrs=(P + 8, P, P, P)), dict(ptrs=(P, P, P + 4, P)),
+    dict(B=0), dict(S=0), dict(S=-3), dict(Hq=0), dict(Hkv=0), dict(Dqk=0), dict(Dv=-1), dict(Hq=6, Hkv=4),
+    dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.1),
+    dict(descale=(1.0, 0.0, 1.0)), dict(descale=(1.0, 1.0, float("nan"))), dict(descale=(-1.0, 1.0, 1.0)),
+    dict(flags=1), dict(B=1 << 20, S=1 << 30, Hq=1 << 10, Hkv=1 << 10),
+])
+def test_invalid_arguments(kw):
+    assert _call(**kw) == fbc.ATTN_ERR_INVALID
+
+
+@pytest.mark.parametrize("kw", [
+    dict(causal=0), dict(dtype=2), dict(dtype=-1), dict(Dqk=64, Dv=64), dict(Dqk=128, Dv=64), dict(Dqk=256, Dv=256),
+])
+def test_unsupported_arguments(kw):
+    assert _call(**kw) == fbc.ATTN_ERR_UNSUPPORTED
+
+
+def test_plain_entry_point_validates_too():
+    assert fbc.attn_fwd(0, P, P, P, 1, 1, 1, 16, 128, 128, 1, 0.1, fbc.ATTN_BF16) == fbc.ATTN_ERR_INVALID
+    assert fbc.attn_fwd(P, P, P, P, 1, 1, 1, 16, 128, 128, 0, 0.1, fbc.ATTN_BF16) == fbc.ATTN_ERR_UNSUPPORTED
+
+
+def test_binding_has_no_cpu_path():
+    """The Python layer only marshals arguments: it refuses CPU tensors rather
+    than computing anything itself."""
+    import torch
+    q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fbc.flash_attn_func(q, q, q)
