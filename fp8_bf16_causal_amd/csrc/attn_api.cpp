@@ -61,6 +61,9 @@ extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
   const int64_t dmax = Dqk > Dv ? Dqk : Dv;
   if ((int64_t)B * S * Hq * dmax * 2 > (INT64_C(1) << 62) || (int64_t)B * S * Hq * dmax * elem > (INT64_C(1) << 62))
     return ATTN_ERR_INVALID;
+  // the kernels address one batch entry of each tensor with 32-bit offsets
+  const int64_t per_batch_max = (int64_t)S * (Hq > Hkv ? Hq : Hkv) * dmax * 2;
+  if (per_batch_max >= (INT64_C(1) << 32)) return ATTN_ERR_INVALID;
   const int64_t nqb = ((int64_t)S + fbc::kBQ - 1) / fbc::kBQ;
   const int64_t grid = (int64_t)B * Hq * nqb;
   if (grid > 0x7fffffff) return ATTN_ERR_INVALID;

@@ -14,6 +14,7 @@
 //    cover K in [0, 64), bytes 16-31 cover K in [64, 128); the scale of
 //    (i, 32-wide K block kb) comes from lane i + 16*kb. D lane (j = l%16, g)
 //    register r holds D[4g + r][j].
+//  * global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l.
 //  * ds_read_b64_tr_b8: within each 16-lane group, lanes 2b and 2b+1 supply
 //    the addresses of the two 8-byte halves of "row" b (b = 0..7); lane c
 //    receives byte c of each of the 8 rows.
@@ -31,6 +32,8 @@
 #include <stdint.h>
 
 namespace fbc {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -110,7 +113,6 @@ __device__ inline float sum_xor32(float x) {
   return as_f(r[0]) + as_f(r[1]);
 }
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ inline v2i lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(lds_u8*)p);
@@ -120,6 +122,50 @@ __device__ inline v4s lds_read_tr16(const uint8_t* p) {
 }
 
 __device__ inline v4i ld_global16(const uint8_t* p) { return *(const v4i*)p; }
+
+// global_load_lds_dwordx4: lane l's 16 bytes from src land at lds_base + 16 l
+// (lds_base is wave-uniform). Completion is tracked by vmcnt.
+__device__ inline void gl_load_lds16(const uint8_t* src, uint8_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(lds_u8*)lds_base, 16,
+                                   0, 0);
+}
+// s_waitcnt vmcnt(0): every vector-memory load of this wave (including
+// direct-to-LDS ones) has completed.
+__device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// Workgroup barrier without a memory fence. __syncthreads() also waits for
+// every outstanding global load of the wave (vmcnt(0)), which would stall each
+// slot on the direct-to-LDS loads still in flight for a later slot. This one
+// waits only for the wave's own LDS operations (no LDS read may still be in
+// flight when another wave overwrites a buffer after the barrier); callers
+// wait_vmem() before the barrier that publishes a direct-to-LDS tile. The
+// memory clobber keeps the compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Direct-to-LDS copy of one key tile. LDS row r has CS 16-byte chunks, the
+// first CD of which hold bytes [0, 16 CD) of key row k0 + key_of(r) of a
+// global array (base g, row_stride bytes per key row); the remaining chunks of
+// the row (padding) receive a duplicate of its first chunk. Rows past the
+// sequence end read row S - 1 (finite data whose keys every stored query masks).
+// The ROWS * CS chunks are written by 1 KiB instructions spread over NW
+// loading waves; `wave` is the caller's index among them (0 .. NW-1).
+// Offsets are 32-bit: the caller guarantees S * row_stride < 2^32.
+template <int ROWS, int CS, int CD, int NW, typename KeyOf>
+__device__ inline void load_tile_lds(const uint8_t* g, uint32_t row_stride, int k0, int S, uint8_t* lds_tile,
+                                     int wave, int lane, KeyOf key_of) {
+  static_assert(ROWS * CS % 64 == 0, "tile must be a whole number of 1 KiB loads");
+  constexpr int kInsts = ROWS * CS / 64;
+  constexpr int kPerWave = (kInsts + NW - 1) / NW;
+#pragma unroll
+  for (int u = 0; u < kPerWave; ++u) {
+    const int i = wave + NW * u;
+    if (kInsts % NW == 0 || i < kInsts) {
+      const int n = i * 64 + lane, r = n / CS, pos = n - r * CS;
+      const int c = pos < CD ? pos : 0;
+      const int j = min(k0 + key_of(r), S - 1);
+      gl_load_lds16(g + ((uint32_t)j * row_stride + 16u * (uint32_t)c), lds_tile + i * 1024);
+    }
+  }
+}
+
 __device__ inline v4i ld_lds16(const uint8_t* p) { return *(const v4i*)p; }
 __device__ inline void st_lds16(uint8_t* p, v4i x) { *(v4i*)p = x; }
 

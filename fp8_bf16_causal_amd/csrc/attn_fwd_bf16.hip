@@ -8,14 +8,17 @@
 //   S = Q K^T, m = running row max, P = 2^((S - m) c) rounded to BF16,
 //   O = sum P V / sum P, rescaled by 2^((m_old - m_new) c) when m rises.
 // Readings: the row sum accumulates the fp32 probabilities (before their BF16
-// rounding); the running max is updated once per key tile.
+// rounding); the reference max is updated per key tile, lazily (only when the
+// tile max exceeds it by more than 8 binades), with an exact rescale then.
 //
 // Tiling (gfx950-specific): 8 waves x 32 query rows per workgroup; K/V tiles
-// of BK keys staged through LDS, double-buffered. S^T = K Q^T and
+// of BK keys staged in LDS by direct-to-LDS loads, double-buffered, with the
+// same two-group ping-pong schedule as the FP8 kernel. S^T = K Q^T and
 // O^T = V^T P^T both run on v_mfma_f32_32x32x16_bf16, so each lane holds one
 // query (l%32): row maxima and sums are in-lane plus one permlane32 swap, and
 // the probabilities feed the P V instruction straight from registers. V stays
-// row-major in LDS; the V^T operand is read with ds_read_b64_tr_b16.
+// row-major in LDS (rows permuted); the V^T operand is read with
+// ds_read_b64_tr_b16.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -25,26 +28,45 @@ template <int DQK, int BK>
 struct Bf16Layout {
   static constexpr int kBK = BK;
   static constexpr int kDv = 128;
-  static constexpr int kNsb = BK / 32;                 // 32-key blocks per tile
-  static constexpr int kKStride = DQK * 2 + 16;        // padded K row (bytes)
-  static constexpr int kVStride = kDv * 2 + 32;        // padded V row (bytes)
-  static constexpr int kKTile = BK * kKStride;
+  static constexpr int kNsb = BK / 32;                // 32-key blocks per tile
+  static constexpr bool kHi = DQK == 192;             // K columns 128..191 kept apart
+  // one 16-byte padding chunk per LDS row: additive chunk offsets, and
+  // consecutive rows start in different bank groups
+  static constexpr int kKLoStride = 272;              // K[:, 0:128]  (256 data bytes)
+  static constexpr int kKHiStride = 144;              // K[:, 128:192] (128 data bytes)
+  static constexpr int kVStride = 272;                // V (256 data bytes)
+  static constexpr int kKLoTile = BK * kKLoStride;
+  static constexpr int kKHiTile = kHi ? BK * kKHiStride : 0;
+  static constexpr int kKTile = kKLoTile + kKHiTile;
   static constexpr int kVTile = BK * kVStride;
-  static constexpr int kStage = kKTile + kVTile;
-  static constexpr int kLoop = 2 * kStage;
+  static constexpr int kLoop = 2 * (kKTile + kVTile);
   static constexpr int kEpi = kWaves * kQW * kOStride;
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
-  static constexpr int kKChunksPerRow = DQK * 2 / 16;
-  static constexpr int kKPerThread = BK * kKChunksPerRow / kThreads;
-  static constexpr int kVPerThread = BK * (kDv * 2 / 16) / kThreads;
 };
 
+// V's LDS row for key k of the tile: inside each group of 16 keys the two
+// 2-bit fields of k swap. One ds_read_b64_tr_b16 pass serves two 16-lane
+// groups that read the same 4 consecutive keys at 32-byte-apart columns; the
+// swap puts those 4 rows 4 bank groups apart under the 272-byte stride.
+__device__ inline int vrow_bf16(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
+
+// Ping-pong schedule, as in the FP8 kernel: slots separated by workgroup
+// barriers, group 1 (waves 4-7) one phase behind group 0 (waves 0-3), so the
+// two waves of a SIMD alternate between
+//   X_t: O^T += V^T P_{t-1}^T, then S_t^T = K_t Q^T   [matrix cores]
+//   Y_t: mask, maxima, rescale, P_t = 2^((S - m) c) -> BF16, row sum  [vector ALU]
+// In slot 2t the group-1 waves issue direct-to-LDS loads of K_{t+1} and V_t and
+// wait for them before the barrier closing slot 2t+1; double buffers suffice.
 template <int DQK, int BK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p) {
   using L = Bf16Layout<DQK, BK>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::kLds];
+  uint8_t* const Kbuf = lds;
+  uint8_t* const Vbuf = lds + 2 * L::kKTile;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is wave-uniform: keep it (and all phase control) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
   const int l32 = lane & 31, g = lane >> 5;
   int b, h, qb;
   map_block(p, blockIdx.x, b, h, qb);
@@ -54,7 +76,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   const int n_tiles = (min(q0 + kBQ, S) + BK - 1) / BK;
   const int wave_tiles = qw0 < S ? (min(qw0 + kQW, S) - 1) / BK + 1 : 0;
 
-  const size_t q_rs = (size_t)p.Hq * DQK * 2, k_rs = (size_t)p.Hkv * DQK * 2, v_rs = (size_t)p.Hkv * L::kDv * 2;
+  const uint32_t q_rs = (uint32_t)p.Hq * DQK * 2, k_rs = (uint32_t)p.Hkv * DQK * 2,
+                 v_rs = (uint32_t)p.Hkv * L::kDv * 2;
   const uint8_t* Qg = (const uint8_t*)p.q + (size_t)b * S * q_rs + (size_t)h * DQK * 2;
   const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * S * k_rs + (size_t)kvh * DQK * 2;
   const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * S * v_rs + (size_t)kvh * L::kDv * 2;
@@ -66,51 +89,44 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
 #pragma unroll
     for (int t = 0; t < DQK / 16; ++t) {
       v4i x = {0, 0, 0, 0};
-      if (qrow < S) x = ld_global16(Qg + (size_t)qrow * q_rs + (16 * t + 8 * g) * 2);
+      if (qrow < S) x = ld_global16(Qg + ((uint32_t)qrow * q_rs + (16 * t + 8 * g) * 2));
       qf[t] = __builtin_bit_cast(v8bf, x);
     }
   }
 
-  v4i kst[L::kKPerThread], vst[L::kVPerThread];
-  auto stage_load = [&](int t) {
-    const int k0 = t * BK;
-#pragma unroll
-    for (int u = 0; u < L::kKPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x / L::kKChunksPerRow, c = x % L::kKChunksPerRow;
-      const int j = k0 + row;
-      kst[u] = j < S ? ld_global16(Kg + (size_t)j * k_rs + 16 * c) : (v4i){0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < L::kVPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x >> 4, c = x & 15;
-      const int j = k0 + row;
-      vst[u] = j < S ? ld_global16(Vg + (size_t)j * v_rs + 16 * c) : (v4i){0, 0, 0, 0};
-    }
+  // Only group 1 issues the direct-to-LDS loads, at the start of its softmax
+  // phase (slot 2t), so that no wave starts a matrix phase behind a burst of
+  // its own memory instructions.
+  constexpr int kLoadWaves = kWaves / 2;
+  const int lw = wave - kLoadWaves;
+  auto identity = [](int r) { return r; };
+  auto issue_k = [&](int t) {
+    uint8_t* Kl = Kbuf + (t & 1) * L::kKTile;
+    load_tile_lds<BK, 17, 16, kLoadWaves>(Kg, k_rs, t * BK, S, Kl, lw, lane, identity);
+    if constexpr (L::kHi)
+      load_tile_lds<BK, 9, 8, kLoadWaves>(Kg + 256, k_rs, t * BK, S, Kl + L::kKLoTile, lw, lane, identity);
   };
-  auto stage_store = [&](int buf) {
-    uint8_t* Kl = lds + buf * L::kStage;
-    uint8_t* Vl = Kl + L::kKTile;
-#pragma unroll
-    for (int u = 0; u < L::kKPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x / L::kKChunksPerRow, c = x % L::kKChunksPerRow;
-      st_lds16(Kl + row * L::kKStride + 16 * c, kst[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < L::kVPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x >> 4, c = x & 15;
-      st_lds16(Vl + row * L::kVStride + 16 * c, vst[u]);
-    }
+  auto issue_v = [&](int t) {
+    uint8_t* Vl = Vbuf + (t & 1) * L::kVTile;
+    load_tile_lds<BK, 17, 16, kLoadWaves>(Vg, v_rs, t * BK, S, Vl, lw, lane, vrow_bf16);
   };
 
-  // V^T operand of v_mfma_f32_32x32x16_bf16, read with ds_read_b64_tr_b16:
-  // lane (d = 32 db + l%32, half g) needs the keys whose probabilities sit in
-  // the P operand: for block sb and step hh, 8(r/4) + 4g + r%4 + 32 sb + 16 hh
-  // for r = 0..7, i.e. 4 consecutive keys at +0 and 4 more at +8.
+  // V^T operand of v_mfma_f32_32x32x16_bf16 via ds_read_b64_tr_b16: lane
+  // (d = 32 db + l%32, half g) needs the keys whose probabilities sit in the P
+  // operand: for block sb, step hh and half eh, keys 32 sb + 16 hh + 8 eh +
+  // 4 g + 0..3. In 16-lane group G (d0 = 32 db + 16 (G & 1), g = G >> 1),
+  // lanes 4 br + w read key ... + br, elements d0 + 4w .. +3; with the row
+  // permutation the per-lane part is (4 br + (G >> 1)) rows and the rest is an
+  // additive offset of (32 sb + 16 hh + 2 eh) rows + 64 db bytes.
   int vrd;
   {
     const int G = lane >> 4, pp = lane & 15, br = pp >> 2, w = pp & 3;
-    vrd = (4 * (G >> 1) + br) * L::kVStride + (16 * (G & 1) + 4 * w) * 2;
+    vrd = (4 * br + (G >> 1)) * L::kVStride + 32 * (G & 1) + 8 * w;
   }
+  // K operand: block sb reads row sb*32 + l32, bytes 32 t16 + 16 g (D columns
+  // 16 t16 + 8 g .. +7)
+  const int krd = l32 * L::kKLoStride + 16 * g;
+  const int khrd = l32 * L::kKHiStride + 16 * g;
 
   v16f oacc[4];
 #pragma unroll
@@ -118,85 +134,141 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   float m = -INFINITY, lsum = 0.0f;
   const float c = p.c;
 
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
+  v16f s[L::kNsb];           // S_t^T, from X_t to Y_t
+  v8bf pf[L::kNsb][2];       // P_t as the B operand of the P V instruction, from Y_t to X_{t+1}
+#pragma unroll
+  for (int sb = 0; sb < L::kNsb; ++sb) pf[sb][0] = pf[sb][1] = (v8bf){};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) stage_load(t + 1);
-    if (t < wave_tiles) {
-      const uint8_t* Kl = lds + buf * L::kStage;
-      const uint8_t* Vl = Kl + L::kKTile;
-      const int k0 = t * BK;
-
-      v16f s[L::kNsb];
+  // X_t: the matrix phase of tile t (P V of tile t-1, then Q K^T of tile t).
+  auto phase_x = [&](int tt) {
+    __builtin_amdgcn_s_setprio(1);
+    const bool do_pv = tt >= 1 && tt - 1 < wave_tiles;
+    const bool do_qk = tt < wave_tiles;
+    const uint8_t* Kl = Kbuf + (tt & 1) * L::kKTile;
+    const uint8_t* Vl = Vbuf + ((tt - 1) & 1) * L::kVTile;
+    // PV step i = (sb * 2 + hh) * 4 + db
+    auto read_v = [&](int i) {
+      const int db = i & 3, hh = (i >> 2) & 1, sb = i >> 3;
+      const uint8_t* vb = Vl + vrd + (32 * sb + 16 * hh) * L::kVStride + 64 * db;
+      const v2i lo = __builtin_bit_cast(v2i, lds_read_tr16(vb));
+      const v2i hi = __builtin_bit_cast(v2i, lds_read_tr16(vb + 2 * L::kVStride));
+      return __builtin_bit_cast(v8bf, (v4i){lo.x, lo.y, hi.x, hi.y});
+    };
+    // QK step i = t16 * kNsb + sb
+    auto read_k = [&](int i) {
+      const int sb = i % L::kNsb, t16 = i / L::kNsb;
+      const uint8_t* kp = t16 < 8 ? Kl + sb * 32 * L::kKLoStride + krd + 32 * t16
+                                  : Kl + L::kKLoTile + sb * 32 * L::kKHiStride + khrd + 32 * (t16 - 8);
+      return __builtin_bit_cast(v8bf, ld_lds16(kp));
+    };
+    constexpr int kPvSteps = L::kNsb * 2 * 4;
+    constexpr int kQkSteps = L::kNsb * (DQK / 16);
+    // S_{tt-1} was consumed by Y_{tt-1}: end its live range (no instruction)
 #pragma unroll
-      for (int sb = 0; sb < L::kNsb; ++sb) s[sb] = (v16f){};
+    for (int sb = 0; sb < L::kNsb; ++sb) asm volatile("" : "=v"(s[sb]));
+    // operand fragments are read two steps ahead of the MFMAs that use them
+    if (do_pv) {
+      v8bf vf[3];
+      vf[0] = read_v(0);
+      vf[1] = read_v(1);
 #pragma unroll
-      for (int t16 = 0; t16 < DQK / 16; ++t16) {
-#pragma unroll
-        for (int sb = 0; sb < L::kNsb; ++sb) {
-          const v4i kx = ld_lds16(Kl + (sb * 32 + l32) * L::kKStride + (16 * t16 + 8 * g) * 2);
-          s[sb] = mfma_32x32x16_bf16(__builtin_bit_cast(v8bf, kx), qf[t16], s[sb]);
-        }
+      for (int i = 0; i < kPvSteps; ++i) {
+        if (i + 2 < kPvSteps) vf[(i + 2) % 3] = read_v(i + 2);
+        oacc[i & 3] = mfma_32x32x16_bf16(vf[i % 3], pf[i >> 3][(i >> 2) & 1], oacc[i & 3]);
+        __builtin_amdgcn_sched_barrier(0);
       }
-
-      if (k0 + BK - 1 > qw0) {
-        const int qi = qw0 + l32;
+    }
+    if (do_qk) {
+      v8bf kf[3];
+      kf[0] = read_k(0);
+      kf[1] = read_k(1);
 #pragma unroll
-        for (int sb = 0; sb < L::kNsb; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > qi) s[sb][r] = -INFINITY;
-          }
+      for (int i = 0; i < kQkSteps; ++i) {
+        if (i + 2 < kQkSteps) kf[(i + 2) % 3] = read_k(i + 2);
+        const int sb = i % L::kNsb;
+        s[sb] = mfma_32x32x16_bf16(kf[i % 3], qf[i / L::kNsb], i < L::kNsb ? (v16f){} : s[sb]);
+        __builtin_amdgcn_sched_barrier(0);
       }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
 
-      float mt = s[0][0];
+  // Y_t: the softmax phase of tile t.
+  auto phase_y = [&](int tt) {
+    const int k0 = tt * BK;
+    if (k0 + BK - 1 > qw0) {  // the tile crosses this wave's diagonal
+      const int qi = qw0 + l32;
 #pragma unroll
       for (int sb = 0; sb < L::kNsb; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
-      mt = max_xor32(mt);
-      const float mn = fmaxf(m, mt);
-      const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
-      m = mn;
-      const float nmc = -mn * c;
-
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-        lsum *= alpha;
-      }
-
-#pragma unroll
-      for (int sb = 0; sb < L::kNsb; ++sb) {
-        float pr[16];
-#pragma unroll
         for (int r = 0; r < 16; ++r) {
-          pr[r] = __builtin_amdgcn_exp2f(fmaf(s[sb][r], c, nmc));
-          lsum += pr[r];
+          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > qi) s[sb][r] = -INFINITY;
         }
+    }
+    float mt = s[0][0];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const v4i pw = {(int)pack_bf16(pr[8 * hh + 0], pr[8 * hh + 1]), (int)pack_bf16(pr[8 * hh + 2], pr[8 * hh + 3]),
-                          (int)pack_bf16(pr[8 * hh + 4], pr[8 * hh + 5]), (int)pack_bf16(pr[8 * hh + 6], pr[8 * hh + 7])};
-          const v8bf pf = __builtin_bit_cast(v8bf, pw);
-          const uint8_t* vb = Vl + vrd + (sb * 32 + 16 * hh) * L::kVStride;
+    for (int sb = 0; sb < L::kNsb; ++sb)
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const v4s lo = lds_read_tr16(vb + db * 64);
-            const v4s hi = lds_read_tr16(vb + db * 64 + 8 * L::kVStride);
-            const v4i vv = {__builtin_bit_cast(v2i, lo).x, __builtin_bit_cast(v2i, lo).y,
-                            __builtin_bit_cast(v2i, hi).x, __builtin_bit_cast(v2i, hi).y};
-            oacc[db] = mfma_32x32x16_bf16(__builtin_bit_cast(v8bf, vv), pf, oacc[db]);
-          }
-        }
+      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[sb][r]);
+    mt = max_xor32(mt);
+    // Lazy running max: the reference m moves (and the accumulators are
+    // rescaled) only when the tile max exceeds it by more than 8 binades;
+    // probabilities up to 2^8 are exact in BF16's range and O / l does not
+    // depend on the reference point.
+    const float mn = (mt - m) * c > 8.0f ? mt : m;
+    const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
+    m = mn;
+    const float nmc = -mn * c;
+    if (__any(alpha != 1.0f)) {
+      // keep this a real branch: the multiplies are skipped on most tiles
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      lsum *= alpha;
+    }
+#pragma unroll
+    for (int sb = 0; sb < L::kNsb; ++sb) {
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(fmaf(s[sb][r], c, nmc));
+        lsum += pr[r];
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const v4i pw = {(int)pack_bf16(pr[8 * hh + 0], pr[8 * hh + 1]), (int)pack_bf16(pr[8 * hh + 2], pr[8 * hh + 3]),
+                        (int)pack_bf16(pr[8 * hh + 4], pr[8 * hh + 5]), (int)pack_bf16(pr[8 * hh + 6], pr[8 * hh + 7])};
+        pf[sb][hh] = __builtin_bit_cast(v8bf, pw);
       }
     }
-    if (t + 1 < n_tiles) stage_store(buf ^ 1);
-    __syncthreads();
+  };
+
+  if (grp == 1) issue_k(0);
+  wait_vmem();
+  lds_barrier();
+
+  // One copy of the slot loop per group (2 slots per iteration): same
+  // barriers in the same slots, simpler live ranges. Group 1 stages tiles.
+  if (grp == 0) {
+    for (int t = 0; t <= n_tiles; ++t) {
+      phase_x(t);                              // slot 2t: X_t
+      lds_barrier();
+      if (t < wave_tiles) phase_y(t);          // slot 2t + 1: Y_t
+      lds_barrier();
+    }
+  } else {
+    for (int t = 0; t <= n_tiles; ++t) {
+      if (t < n_tiles) {                       // slot 2t: Y_{t-1}
+        if (t + 1 < n_tiles) issue_k(t + 1);
+        issue_v(t);
+      }
+      if (t >= 1 && t - 1 < wave_tiles) phase_y(t - 1);
+      lds_barrier();
+      phase_x(t);                              // slot 2t + 1: X_t
+      if (t < n_tiles) wait_vmem();            // slot 2t's loads are first read in slot 2t + 2
+      lds_barrier();
+    }
   }
 
   // ---- epilogue: lanes l and l^32 hold partial sums of one query.
@@ -215,14 +287,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   }
   __syncthreads();
   if (wave_tiles > 0) {
-    uint8_t* Og = (uint8_t*)p.out;
+    uint8_t* Og = (uint8_t*)p.out + ((size_t)b * S * p.Hq + h) * (L::kDv * 2);
+    const uint32_t o_rs = (uint32_t)p.Hq * L::kDv * 2;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = lane + 64 * u, row = x >> 4, cc = x & 15;
       const int qrow = qw0 + row;
-      if (qrow < S)
-        *(v4i*)(Og + (((size_t)b * S + qrow) * p.Hq + h) * (L::kDv * 2) + 16 * cc) =
-            ld_lds16(Ol + row * kOStride + 16 * cc);
+      if (qrow < S) *(v4i*)(Og + ((uint32_t)qrow * o_rs + 16 * cc)) = ld_lds16(Ol + row * kOStride + 16 * cc);
     }
   }
 }

@@ -14,19 +14,22 @@
 //    scaled matrix instruction applies 2^-k through its E8M0 operand scale;
 //  * the row sum is taken over the rounded probabilities with one extra
 //    matrix instruction against an all-ones operand (16 rows), and the output
-//    is divided by it.
+//    is divided by it;
+//  * two waves share each SIMD and ping-pong: one issues matrix instructions
+//    while the other computes probabilities, in an order fixed by the
+//    instruction stream.
 //
 // Readings where the pages leave a step open: C = 55.63 (minimax constant,
 // the only narrow window meeting the pages' 7.5 percent bound); the block
 // exponent k = floor(8 - t_max), t_max the block's largest log2 probability
-// relative to the running max, capped at 127 (E8M0 range); the running max is
-// updated once per 128-key tile and the accumulators are rescaled exactly
-// when it rises.
+// relative to the reference max, kept in [0, 127] (E8M0 range); the reference
+// max is updated per 128-key tile, lazily: only when the tile max exceeds it
+// by more than 8 binades, and the accumulators are rescaled exactly then.
 //
 // Tiling (gfx950-specific, not from the pages): a workgroup of 8 waves owns
 // 256 consecutive query rows of one head; each wave owns 32 rows. K and V
-// tiles of 128 keys are staged through LDS, double-buffered, and shared by the
-// 8 waves.
+// tiles of 128 keys are staged in LDS, double-buffered, and shared by the 8
+// waves.
 //  * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (neutral scales): each
 //    lane then holds one query (l%32) and 64 of the tile's keys, so row maxima
 //    are in-lane plus one permlane32 swap.
@@ -38,43 +41,72 @@
 //  * The same P operand against an all-ones A operand gives the rounded row
 //    sum: one 16x16x128 instruction per 16 queries and 128 keys, 1/16 of the
 //    P V work (the pages' +6 percent).
-//  * V stays row-major in LDS (16-byte chunks XOR-swizzled by row) and the
-//    V^T operand is read with ds_read_b64_tr_b8.
+//  * K and V are copied global -> LDS by direct-to-LDS loads (no staging
+//    registers) into padded row-major tiles; V's rows are permuted so that
+//    the transposing reads (ds_read_b64_tr_b8) building the V^T operand are
+//    free of bank conflicts.
 #include "attn_common.h"
 #include "attn_launch.h"
 
 namespace fbc {
 
 constexpr float kLeanPC = 55.63f;
+// lazy running-max threshold, in binades (log2 units)
+constexpr float kLazyLog2 = 8.0f;
 
 template <int DQK>
 struct Fp8Layout {
-  static constexpr int kBK = 128;                // keys per tile
+  static constexpr int kBK = 128;                     // keys per tile
   static constexpr int kDv = 128;
-  static constexpr int kKStride = DQK + 16;      // padded K row in LDS (bytes)
-  static constexpr int kVStride = kDv;           // V row in LDS, chunk-swizzled
-  static constexpr int kKTile = kBK * kKStride;
+  static constexpr bool kHi = DQK == 192;             // K columns 128..191 kept apart
+  // LDS rows carry one 16-byte padding chunk, so that a row's chunks sit at
+  // additive offsets and consecutive rows start in different bank groups.
+  static constexpr int kKLoStride = 144;              // K[:, 0:128]
+  static constexpr int kKHiStride = 80;               // K[:, 128:192]
+  static constexpr int kVStride = 144;                // V
+  static constexpr int kKLoTile = kBK * kKLoStride;
+  static constexpr int kKHiTile = kHi ? kBK * kKHiStride : 0;
+  static constexpr int kKTile = kKLoTile + kKHiTile;
   static constexpr int kVTile = kBK * kVStride;
-  static constexpr int kStage = kKTile + kVTile;
-  static constexpr int kLoop = 2 * kStage;
+  static constexpr int kLoop = 2 * (kKTile + kVTile);
   static constexpr int kEpi = kWaves * kQW * kOStride;
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
-  static constexpr int kKChunksPerRow = DQK / 16;
-  static constexpr int kKPerThread = kBK * kKChunksPerRow / kThreads;
-  static constexpr int kVPerThread = kBK * (kDv / 16) / kThreads;
 };
 
-// 16-byte chunk swizzle of V rows: rows r..r+3 and r+8..r+11 (r % 16 in {0, 4})
-// land in 8 different bank groups, which is the row set one ds_read_b64_tr_b8
-// group reads.
-__device__ inline int vswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// V's LDS row for key k of the tile: within each 64-key half, keys 32..63
+// trade places in groups of four (bit 2 flips when bit 5 is set). One
+// ds_read_b64_tr_b8 pass serves two 16-lane groups whose keys are 32 apart;
+// with the 144-byte stride their 16 rows then fall in 16 distinct bank groups.
+__device__ inline int vrow_fp8(int k) { return k ^ (((k >> 5) & 1) << 2); }
 
+// Ping-pong schedule. The workgroup's 8 waves form two groups (waves w and
+// w + 4 share a SIMD). Time is cut into slots separated by workgroup
+// barriers; in slot p group 0 runs its phase p and group 1 its phase p - 1.
+// A wave's phases alternate
+//   X_t: O^T += V^T P_{t-1}^T (and the row-sum MFMA), then S_t^T = K_t Q^T   [matrix cores]
+//   Y_t: softmax of S_t: maxima, block exponents, Lean P codes, rescale       [vector ALU]
+// so on every SIMD one wave issues matrix instructions while its partner
+// computes probabilities, and they swap at the next barrier.
+// [spbcomputers.ru ZYFA article and captivela.com "Zyphra Luncurkan ZYFA",
+// sections on the three techniques: two waves per SIMD, one on the matrix
+// cores while the other computes probabilities, order enforced by the
+// instruction stream because the hardware does not track MFMA completion.]
+//
+// K/V staging: in slot 2t the group-1 waves issue direct-to-LDS loads of K_{t+1}
+// and V_t into the buffers last read in slot 2t-1, and wait for them before
+// the barrier that closes slot 2t+1 (two slots of latency cover). K_t is read
+// in slots 2t and 2t+1, V_t in slots 2t+2 and 2t+3, so two buffers of each
+// suffice.
 template <int DQK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p) {
   using L = Fp8Layout<DQK>;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[L::kLds];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[L::kLds];
+  uint8_t* const Kbuf = lds;                    // 2 x kKTile
+  uint8_t* const Vbuf = lds + 2 * L::kKTile;    // 2 x kVTile
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is wave-uniform: keep it (and all phase control) in scalar registers
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;
   const int l32 = lane & 31, g = lane >> 5;
   int b, h, qb;
   map_block(p, blockIdx.x, b, h, qb);
@@ -84,7 +116,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   const int n_tiles = (min(q0 + kBQ, S) + L::kBK - 1) / L::kBK;
   const int wave_tiles = qw0 < S ? (min(qw0 + kQW, S) - 1) / L::kBK + 1 : 0;
 
-  const size_t q_rs = (size_t)p.Hq * DQK, k_rs = (size_t)p.Hkv * DQK, v_rs = (size_t)p.Hkv * L::kDv;
+  const uint32_t q_rs = (uint32_t)p.Hq * DQK, k_rs = (uint32_t)p.Hkv * DQK, v_rs = (uint32_t)p.Hkv * L::kDv;
   const uint8_t* Qg = (const uint8_t*)p.q + (size_t)b * S * q_rs + (size_t)h * DQK;
   const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * S * k_rs + (size_t)kvh * DQK;
   const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * S * v_rs + (size_t)kvh * L::kDv;
@@ -98,7 +130,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     for (int t = 0; t < DQK / 64; ++t) {
       v4i lo = {0, 0, 0, 0}, hi = {0, 0, 0, 0};
       if (qrow < S) {
-        const uint8_t* src = Qg + (size_t)qrow * q_rs + 64 * t + 16 * g;
+        const uint8_t* src = Qg + ((uint32_t)qrow * q_rs + 64 * t + 16 * g);
         lo = ld_global16(src);
         hi = ld_global16(src + 32);
       }
@@ -106,51 +138,39 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     }
   }
 
-  // K/V staging: global -> registers -> LDS, one tile ahead.
-  v4i kst[L::kKPerThread], vst[L::kVPerThread];
-  auto stage_load = [&](int t) {
-    const int k0 = t * L::kBK;
-#pragma unroll
-    for (int u = 0; u < L::kKPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x / L::kKChunksPerRow, c = x % L::kKChunksPerRow;
-      const int j = k0 + row;
-      kst[u] = j < S ? ld_global16(Kg + (size_t)j * k_rs + 16 * c) : (v4i){0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < L::kVPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x >> 3, c = x & 7;
-      const int j = k0 + row;
-      vst[u] = j < S ? ld_global16(Vg + (size_t)j * v_rs + 16 * c) : (v4i){0, 0, 0, 0};
-    }
+  // Only group 1 issues the direct-to-LDS loads, at the start of its softmax
+  // phase (slot 2t), so that no wave starts a matrix phase behind a burst of
+  // its own memory instructions.
+  constexpr int kLoadWaves = kWaves / 2;
+  const int lw = wave - kLoadWaves;
+  auto identity = [](int r) { return r; };
+  auto issue_k = [&](int t) {
+    uint8_t* Kl = Kbuf + (t & 1) * L::kKTile;
+    load_tile_lds<L::kBK, 9, 8, kLoadWaves>(Kg, k_rs, t * L::kBK, S, Kl, lw, lane, identity);
+    if constexpr (L::kHi)
+      load_tile_lds<L::kBK, 5, 4, kLoadWaves>(Kg + 128, k_rs, t * L::kBK, S, Kl + L::kKLoTile, lw, lane, identity);
   };
-  auto stage_store = [&](int buf) {
-    uint8_t* Kl = lds + buf * L::kStage;
-    uint8_t* Vl = Kl + L::kKTile;
-#pragma unroll
-    for (int u = 0; u < L::kKPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x / L::kKChunksPerRow, c = x % L::kKChunksPerRow;
-      st_lds16(Kl + row * L::kKStride + 16 * c, kst[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < L::kVPerThread; ++u) {
-      const int x = tid + kThreads * u, row = x >> 3, c = x & 7;
-      st_lds16(Vl + row * L::kVStride + ((c ^ vswz(row)) << 4), vst[u]);
-    }
+  auto issue_v = [&](int t) {
+    uint8_t* Vl = Vbuf + (t & 1) * L::kVTile;
+    load_tile_lds<L::kBK, 9, 8, kLoadWaves>(Vg, v_rs, t * L::kBK, S, Vl, lw, lane, vrow_fp8);
   };
 
   // Per-lane LDS offsets of the four ds_read_b64_tr_b8 reads that build the
-  // V^T operand of one 16x16x128 instruction (d-block 0; d-block db is the
-  // same offset XOR (db << 4)). Read j covers operand bytes 8j .. 8j+7; its
-  // 8 rows are the keys whose P codes sit in those bytes of the P operand.
+  // V^T operand of one 16x16x128 instruction (d-block 0; d-block db adds
+  // 16 db). Read j covers operand bytes 8j .. 8j+7; its 8 rows are the keys
+  // whose P codes sit in those bytes of the P operand.
   int vrd[4];
   {
     const int g16 = lane >> 4, pp = lane & 15, bb = pp >> 1, hh = pp & 1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = 64 * (j >> 1) + 32 * (g16 & 1) + 4 * (g16 >> 1) + 16 * (j & 1) + 8 * (bb >> 2) + (bb & 3);
-      vrd[j] = row * L::kVStride + 8 * hh + (vswz(row) << 4);
+      const int key = 64 * (j >> 1) + 32 * (g16 & 1) + 4 * (g16 >> 1) + 16 * (j & 1) + 8 * (bb >> 2) + (bb & 3);
+      vrd[j] = vrow_fp8(key) * L::kVStride + 8 * hh;
     }
   }
+  // K operand: block sb reads row sb*32 + l32, chunks 4 t6 + g and 4 t6 + 2 + g
+  const int krd = l32 * L::kKLoStride + 16 * g;
+  const int khrd = l32 * L::kKHiStride + 16 * g;
 
   v4f oacc[8][2];
   v4f lacc[2];
@@ -159,135 +179,191 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   lacc[0] = lacc[1] = (v4f){0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;  // running max of the raw scores of query qw0 + l32
   const float c = p.c, c8 = 8.0f * p.c;
-  const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                    0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
 
-  stage_load(0);
-  stage_store(0);
-  __syncthreads();
+  v16f s[4];     // S_t^T, from X_t to Y_t
+  v8i P[2];      // P_t codes in the 16x16x128 B layout, from Y_t to X_{t+1}
+  int sc0 = 127, sc1 = 127;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) P[q] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < n_tiles) stage_load(t + 1);
-    if (t < wave_tiles) {
-      const uint8_t* Kl = lds + buf * L::kStage;
-      const uint8_t* Vl = Kl + L::kKTile;
-      const int k0 = t * L::kBK;
-
-      // ---- S^T = K Q^T: 4 blocks of 32 keys x 32 queries
-      v16f s[4];
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) s[sb] = (v16f){};
-#pragma unroll
-      for (int t6 = 0; t6 < DQK / 64; ++t6) {
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb) {
-          const uint8_t* kp = Kl + (sb * 32 + l32) * L::kKStride + 64 * t6 + 16 * g;
-          const v4i lo = ld_lds16(kp), hi = ld_lds16(kp + 32);
-          const v8i kf = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          s[sb] = mfma_32x32x64_fp8(kf, qf[t6], s[sb], 127, 127);
-        }
-      }
-
-      // ---- causal mask on the tile that crosses this wave's diagonal
-      if (k0 + L::kBK - 1 > qw0) {
-        const int qi = qw0 + l32;
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > qi) s[sb][r] = -INFINITY;
-          }
-      }
-
-      // ---- per-(row, 64-key block) maxima and the running max
-      float ma = s[0][0], mb = s[2][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) {
-        ma = fmaxf(ma, s[0][r]);
-        mb = fmaxf(mb, s[2][r]);
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        ma = fmaxf(ma, s[1][r]);
-        mb = fmaxf(mb, s[3][r]);
-      }
-      ma = max_xor32(ma);
-      mb = max_xor32(mb);
-      const float mn = fmaxf(m, fmaxf(ma, mb));
-      const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
-      m = mn;
-
-      // ---- block exponents: the block max lands in (2^7, 2^8]
-      const float ka = fminf(floorf(8.0f - (ma - mn) * c), 127.0f);
-      const float kb = fminf(floorf(8.0f - (mb - mn) * c), 127.0f);
-      const float bias_a = fmaf(-c8, mn, kLeanPC + 8.0f * ka);
-      const float bias_b = fmaf(-c8, mn, kLeanPC + 8.0f * kb);
-
-      // ---- Lean P: code = u8(8 c s + C + 8k - 8 c m), four codes per dword
-      uint32_t X[4][4];
-#pragma unroll
-      for (int sb = 0; sb < 4; ++sb) {
-        const float bias = sb < 2 ? bias_a : bias_b;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          uint32_t w = 0;
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 0], c8, bias), 0, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 1], c8, bias), 1, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 2], c8, bias), 2, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 3], c8, bias), 3, w);
-          X[sb][v] = w;
-        }
-      }
-
-      // ---- regroup into the 16x16x128 B-operand layout: P[Q] serves queries
-      // qw0 + 16Q .. +15; bytes 0-15 = keys 0..63, bytes 16-31 = keys 64..127.
-      v8i P[2];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        auto pa = __builtin_amdgcn_permlane16_swap(X[0][v], X[1][v], false, false);
-        auto pb = __builtin_amdgcn_permlane16_swap(X[2][v], X[3][v], false, false);
-        P[0][v] = (int)pa[0];
-        P[1][v] = (int)pa[1];
-        P[0][4 + v] = (int)pb[0];
-        P[1][4 + v] = (int)pb[1];
-      }
-      // E8M0 scale of P: lane i + 16*kb carries (query i of the block, 32-key
-      // group kb); groups 0-1 are the first 64-key block, 2-3 the second.
-      const uint32_t scu = (uint32_t)(127 - (int)(lane < 32 ? ka : kb));
-      auto scp = __builtin_amdgcn_permlane16_swap(scu, scu, false, false);
-      const int sc0 = (int)scp[0], sc1 = (int)scp[1];
-
-      // ---- rescale the accumulators when the running max rose
-      auto ap = __builtin_amdgcn_permlane16_swap(as_u(alpha), as_u(alpha), false, false);
-      const float a0 = as_f(ap[0]), a1 = as_f(ap[1]);
-      if (__any(alpha != 1.0f)) {
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          oacc[db][0] *= a0;
-          oacc[db][1] *= a1;
-        }
-        lacc[0] *= a0;
-        lacc[1] *= a1;
-      }
-
-      // ---- O^T += V^T P^T and the rounded row sum
+  // X_t: the matrix phase of tile t (P V of tile t-1, then Q K^T of tile t).
+  auto phase_x = [&](int tt) {
+    // ================= X_tt: matrix phase
+    // Operand fragments are read two steps ahead of the MFMAs that use them;
+    // scheduling barriers keep the compiler from hoisting every LDS read of
+    // the phase to its top.
+    __builtin_amdgcn_s_setprio(1);
+    const bool do_pv = tt >= 1 && tt - 1 < wave_tiles;
+    const bool do_qk = tt < wave_tiles;
+    const uint8_t* Kl = Kbuf + (tt & 1) * L::kKTile;
+    const uint8_t* Vl = Vbuf + ((tt - 1) & 1) * L::kVTile;
+    auto read_v = [&](int db) {
+      const v2i r0 = lds_read_tr8(Vl + vrd[0] + 16 * db);
+      const v2i r1 = lds_read_tr8(Vl + vrd[1] + 16 * db);
+      const v2i r2 = lds_read_tr8(Vl + vrd[2] + 16 * db);
+      const v2i r3 = lds_read_tr8(Vl + vrd[3] + 16 * db);
+      return (v8i){r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+    };
+    // QK step i = t6 * 4 + sb: K rows sb*32 + l32, bytes 64 t6 + 16 g and +32
+    auto read_k = [&](int i) {
+      const int sb = i & 3, t6 = i >> 2;
+      const uint8_t* kp = t6 < 2 ? Kl + sb * 32 * L::kKLoStride + krd + 64 * t6
+                                 : Kl + L::kKLoTile + sb * 32 * L::kKHiStride + khrd;
+      const v4i lo = ld_lds16(kp), hi = ld_lds16(kp + 32);
+      return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    constexpr int kQkSteps = 4 * (DQK / 64);
+    // S_{tt-1} was consumed by Y_{tt-1}: end its live range here (an empty
+    // asm definition, no instruction) so it does not occupy registers
+    // through the P V half of this phase.
+    asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
+    if (do_pv) {
+      v8i vf[3];
+      vf[0] = read_v(0);
+      vf[1] = read_v(1);
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        const v2i r0 = lds_read_tr8(Vl + (vrd[0] ^ (db << 4)));
-        const v2i r1 = lds_read_tr8(Vl + (vrd[1] ^ (db << 4)));
-        const v2i r2 = lds_read_tr8(Vl + (vrd[2] ^ (db << 4)));
-        const v2i r3 = lds_read_tr8(Vl + (vrd[3] ^ (db << 4)));
-        const v8i vf = {r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-        oacc[db][0] = mfma_16x16x128_fp8(vf, P[0], oacc[db][0], 127, sc0);
-        oacc[db][1] = mfma_16x16x128_fp8(vf, P[1], oacc[db][1], 127, sc1);
+        if (db + 2 < 8) vf[(db + 2) % 3] = read_v(db + 2);
+        oacc[db][0] = mfma_16x16x128_fp8(vf[db % 3], P[0], oacc[db][0], 127, sc0);
+        oacc[db][1] = mfma_16x16x128_fp8(vf[db % 3], P[1], oacc[db][1], 127, sc1);
+        __builtin_amdgcn_sched_barrier(0);
       }
+      const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
       lacc[0] = mfma_16x16x128_fp8(ones, P[0], lacc[0], 127, sc0);
       lacc[1] = mfma_16x16x128_fp8(ones, P[1], lacc[1], 127, sc1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (t + 1 < n_tiles) stage_store(buf ^ 1);
-    __syncthreads();
+    if (do_qk) {
+      v8i kf[3];
+      kf[0] = read_k(0);
+      kf[1] = read_k(1);
+#pragma unroll
+      for (int i = 0; i < kQkSteps; ++i) {
+        if (i + 2 < kQkSteps) kf[(i + 2) % 3] = read_k(i + 2);
+        s[i & 3] = mfma_32x32x64_fp8(kf[i % 3], qf[i >> 2], i < 4 ? (v16f){} : s[i & 3], 127, 127);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Y_t: the softmax phase of tile t.
+  auto phase_y = [&](int tt) {
+    // ================= Y_tt: softmax phase
+    const int k0 = tt * L::kBK;
+    if (k0 + L::kBK - 1 > qw0) {  // the tile crosses this wave's diagonal
+      const int qi = qw0 + l32;
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > qi) s[sb][r] = -INFINITY;
+        }
+    }
+    // per-(row, 64-key block) maxima and the running max
+    float ma = s[0][0], mb = s[2][0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      ma = fmaxf(ma, s[0][r]);
+      mb = fmaxf(mb, s[2][r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      ma = fmaxf(ma, s[1][r]);
+      mb = fmaxf(mb, s[3][r]);
+    }
+    ma = max_xor32(ma);
+    mb = max_xor32(mb);
+    // Lazy running max: the reference m moves (and the accumulators are
+    // rescaled) only when the tile max exceeds it by more than kLazyLog2
+    // binades; otherwise probabilities up to 2^kLazyLog2 are encoded relative
+    // to the old m, which the per-block exponent absorbs (k >= 0 keeps every
+    // code <= 120). O / l does not depend on the reference point.
+    const float mt = fmaxf(ma, mb);
+    const float mn = (mt - m) * c > kLazyLog2 ? mt : m;
+    const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
+    m = mn;
+    // block exponents: the block max lands in (2^7, 2^8]
+    const float ka = fminf(fmaxf(floorf(8.0f - (ma - mn) * c), 0.0f), 127.0f);
+    const float kb = fminf(fmaxf(floorf(8.0f - (mb - mn) * c), 0.0f), 127.0f);
+    const float bias_a = fmaf(-c8, mn, kLeanPC + 8.0f * ka);
+    const float bias_b = fmaf(-c8, mn, kLeanPC + 8.0f * kb);
+    // Lean P: code = u8(8 c s + C + 8k - 8 c m), four codes per dword
+    uint32_t X[4][4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const float bias = sb < 2 ? bias_a : bias_b;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        uint32_t w = 0;
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 0], c8, bias), 0, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 1], c8, bias), 1, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 2], c8, bias), 2, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 3], c8, bias), 3, w);
+        X[sb][v] = w;
+      }
+    }
+    // regroup into the 16x16x128 B-operand layout: P[Q] serves queries
+    // qw0 + 16Q .. +15; bytes 0-15 = keys 0..63, bytes 16-31 = keys 64..127
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      auto pa = __builtin_amdgcn_permlane16_swap(X[0][v], X[1][v], false, false);
+      auto pb = __builtin_amdgcn_permlane16_swap(X[2][v], X[3][v], false, false);
+      P[0][v] = (int)pa[0];
+      P[1][v] = (int)pa[1];
+      P[0][4 + v] = (int)pb[0];
+      P[1][4 + v] = (int)pb[1];
+    }
+    // E8M0 scale of P: lane i + 16*kb carries (query i of the block,
+    // 32-key group kb); groups 0-1 are the first 64-key block, 2-3 the second
+    const uint32_t scu = (uint32_t)(127 - (int)(lane < 32 ? ka : kb));
+    auto scp = __builtin_amdgcn_permlane16_swap(scu, scu, false, false);
+    sc0 = (int)scp[0];
+    sc1 = (int)scp[1];
+    // rescale the accumulators when the running max rose
+    auto ap = __builtin_amdgcn_permlane16_swap(as_u(alpha), as_u(alpha), false, false);
+    const float a0 = as_f(ap[0]), a1 = as_f(ap[1]);
+    if (__any(alpha != 1.0f)) {
+      // keep this a real branch: the multiplies are skipped on most tiles
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        oacc[db][0] *= a0;
+        oacc[db][1] *= a1;
+      }
+      lacc[0] *= a0;
+      lacc[1] *= a1;
+    }
+  };
+
+  if (grp == 1) issue_k(0);
+  wait_vmem();
+  lds_barrier();
+
+  // Each group runs its own copy of the slot loop (2 slots per iteration), so
+  // that S never has to stay live across the loop's back edge in group 0 and
+  // P never in group 1. Both copies execute the same barriers in the same
+  // slots; group 1 also stages the tiles.
+  if (grp == 0) {
+    for (int t = 0; t <= n_tiles; ++t) {
+      phase_x(t);                              // slot 2t: X_t
+      lds_barrier();
+      if (t < wave_tiles) phase_y(t);          // slot 2t + 1: Y_t
+      lds_barrier();
+    }
+  } else {
+    for (int t = 0; t <= n_tiles; ++t) {
+      if (t < n_tiles) {                       // slot 2t: Y_{t-1}
+        if (t + 1 < n_tiles) issue_k(t + 1);
+        issue_v(t);
+      }
+      if (t >= 1 && t - 1 < wave_tiles) phase_y(t - 1);
+      lds_barrier();
+      phase_x(t);                              // slot 2t + 1: X_t
+      if (t < n_tiles) wait_vmem();            // slot 2t's loads are first read in slot 2t + 2
+      lds_barrier();
+    }
   }
 
   // ---- epilogue: O / l * dv -> BF16, staged through LDS for coalesced rows.
@@ -309,14 +385,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   }
   __syncthreads();
   if (wave_tiles > 0) {
-    uint8_t* Og = (uint8_t*)p.out;
+    uint8_t* Og = (uint8_t*)p.out + ((size_t)b * S * p.Hq + h) * (L::kDv * 2);
+    const uint32_t o_rs = (uint32_t)p.Hq * L::kDv * 2;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int x = lane + 64 * u, row = x >> 4, cc = x & 15;
       const int qrow = qw0 + row;
-      if (qrow < S)
-        *(v4i*)(Og + (((size_t)b * S + qrow) * p.Hq + h) * (L::kDv * 2) + 16 * cc) =
-            ld_lds16(Ol + row * kOStride + 16 * cc);
+      if (qrow < S) *(v4i*)(Og + ((uint32_t)qrow * o_rs + 16 * cc)) = ld_lds16(Ol + row * kOStride + 16 * cc);
     }
   }
 }

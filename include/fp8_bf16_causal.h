@@ -60,7 +60,8 @@ enum {
   /* a null or misaligned pointer (q, k, v, out must be 16-byte aligned), a
    * size <= 0, Hq not a multiple of Hkv, scale negative or not finite, a
    * descale factor <= 0 or not finite, a non-zero flags word, or sizes whose
-   * products (tensor bytes, workgroup count) overflow the index types */
+   * products overflow the index types (one batch entry of q, k, v or out must
+   * stay below 4 GiB; the workgroup count B*Hq*ceil(S/256) below 2^31) */
   ATTN_ERR_INVALID = -1,
   /* causal == 0 (the method is causal-only), an unknown dtype, a head-dim
    * pair other than (Dqk, Dv) = (128, 128) or (192, 128), or a current device

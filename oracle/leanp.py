@@ -37,8 +37,10 @@ Readings where the pages leave a step open (each listed in the design doc):
 * The integer convert rounds half to even and saturates to [0, 255]; codes are
   then capped at 126 (the largest finite e4m3 code).
 * Keys are processed in tiles of 128 (the unit the pages cost: 32 queries by
-  128 keys), the running max is updated once per tile, and the accumulated
-  output and sum are rescaled by 2**(m_old - m_new) exactly when it rises.
+  128 keys); the reference max is updated once per tile and the accumulated
+  output and sum are rescaled by 2**(m_old - m_new) exactly when it moves.
+  Optionally (lazy_log2 > 0) it moves only when a tile's max exceeds it by
+  more than lazy_log2 binades, as the GPU kernels do with 8.
 """
 from __future__ import annotations
 
@@ -110,16 +112,16 @@ def e4m3_round_rne(x) -> np.ndarray:
 
 
 def block_exponent(t_max) -> np.ndarray:
-    """k = floor(8 - t_max), capped to [.., 127]; t_max = -inf (an all-masked
+    """k = floor(8 - t_max), kept in [0, 127]; t_max = -inf (an all-masked
     block) gives 127."""
     t = np.asarray(t_max, dtype=np.float64)
     k = np.floor(8.0 - t)
-    return np.minimum(np.where(np.isfinite(k), k, 127.0), 127.0).astype(np.int64)
+    return np.clip(np.where(np.isfinite(k), k, 127.0), 0.0, 127.0).astype(np.int64)
 
 
 def leanp_attention_row(z: np.ndarray, vrows: np.ndarray, C: float = LEANP_C, rounding: str = "rne",
                         block_scale: bool = True, exact_p: bool = False,
-                        tile_keys: int = TILE_KEYS) -> tuple[np.ndarray, float]:
+                        tile_keys: int = TILE_KEYS, lazy_log2: float = 0.0) -> tuple[np.ndarray, float]:
     """One query row of the FP8 softmax model.
 
     z: log2-domain scores z_j = s_j * log2(e) of the visible keys, in key order
@@ -131,6 +133,9 @@ def leanp_attention_row(z: np.ndarray, vrows: np.ndarray, C: float = LEANP_C, ro
     probabilities in [0, 1] are encoded, as an unscaled FP8 softmax would;
     exact_p=True replaces the Lean P code with exact e4m3 rounding of 2**x.
     tile_keys: keys per running-max update (a multiple of the 64-key block).
+    lazy_log2: the reference max moves to a tile's max only when that max
+      exceeds it by more than this many binades (0: on every rise). Any value
+      gives the same exact output; it changes which rounding each code sees.
     """
     n = z.shape[0]
     dv = vrows.shape[1]
@@ -139,7 +144,8 @@ def leanp_attention_row(z: np.ndarray, vrows: np.ndarray, C: float = LEANP_C, ro
     o = np.zeros(dv, dtype=np.float64)
     for t0 in range(0, n, tile_keys):
         zt = z[t0:t0 + tile_keys]
-        m_new = max(m, float(np.max(zt)))
+        tmax = float(np.max(zt))
+        m_new = tmax if (m == -np.inf or tmax - m > lazy_log2) else m
         alpha = 0.0 if m == -np.inf else 2.0 ** (m - m_new)
         l *= alpha
         o *= alpha

@@ -151,3 +151,23 @@ def test_roofline_figures(golden):
     # a 16-wide ones operand for the row sum costs 16 / (Dqk + Dv) extra matrix work
     assert round(16 / (128 + 128), 2) == golden["rowsum_extra_matrix_work"]["value"]
     assert golden["block_keys"]["value"] == leanp.BLOCK_KEYS
+
+
+def test_lazy_reference_max_keeps_the_result():
+    """Moving the reference max only on rises of more than 8 binades changes
+    which rounding each code sees, not the attention being approximated: both
+    variants meet the FP8 bar against exact attention, codes stay <= 120."""
+    inp = synth.make_inputs(B=1, S=900, Hq=2, Hkv=1, Dqk=128, Dv=128, dtype="fp8", seed=17, structure="peaked")
+    qd, kd, vd, dv = _dequant(inp)
+    rows = _rows(900, 2, 80, 3)
+    ref = _exact(inp, rows)
+    vmax = np.abs(vd).max() * dv
+    eager = _err(leanp.leanp_attention(qd, kd, vd, inp.scale, dv, rows=rows), ref, vmax)
+    lazy = _err(leanp.leanp_attention(qd, kd, vd, inp.scale, dv, rows=rows, lazy_log2=8.0), ref, vmax)
+    assert eager[0] <= 4e-2 and lazy[0] <= 4e-2 and lazy[1] <= 0.1
+    assert abs(lazy[0] - eager[0]) < 0.5 * eager[0]
+    # with a stale reference the block max sits up to 8 binades above it; the
+    # block exponent is then >= 0 and the code still <= 120
+    t = np.linspace(0.0, 8.0, 1001)
+    k = leanp.block_exponent(t)
+    assert np.all(k >= 0) and np.all(leanp.leanp_code(t + k) <= 120)
