@@ -166,6 +166,78 @@ __device__ inline void load_tile_lds(const uint8_t* g, uint32_t row_stride, int 
   }
 }
 
+// Buffer resource (raw, no stride) over `bytes` bytes from `base`. The
+// hardware range-checks every lane of a buffer load against it: lanes at or
+// past the end read zero instead of memory. Word 3 is the gfx9 default
+// (32-bit data format).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ inline rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// buffer_load_dwordx4 ... lds: lane l's 16 bytes from voff land at
+// lds_base + 16 l (lds_base wave-uniform); out-of-range lanes write zeros.
+__device__ inline void buf_load_lds16(rsrc_t r, uint32_t voff, uint8_t* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_u8*)lds_base, 16,
+                                           (int)voff, 0, 0, 0);
+}
+
+// Direct-to-LDS copy of a key tile through a buffer resource whose range ends
+// at the sequence's last row, so rows past it arrive as zeros. Same LDS row
+// format as load_tile_lds (CS chunks per row, the first CD of them data, the
+// rest a copy of chunk 0). The per-lane source offsets are computed once, so
+// issuing a tile costs no vector instructions. The kInsts 1 KiB instructions
+// are dealt round-robin to the NW waves; the remainder goes to the waves
+// whose (wave + ROT) % NW is below it, so that loaders with different ROT
+// balance each other.
+template <int ROWS, int CS, int CD, int NW, int ROT>
+struct TileLoader {
+  static constexpr int kInsts = ROWS * CS / 64;
+  static constexpr int kFull = kInsts / NW;
+  static constexpr int kRem = kInsts % NW;
+  static constexpr int kRegs = kFull + (kRem ? 1 : 0);
+  static_assert(ROWS * CS % 64 == 0, "tile must be a whole number of 1 KiB loads");
+  uint32_t off[kRegs];
+  int wave;
+  int rem_inst;  // index of this wave's remainder instruction, or -1 (wave-uniform)
+
+  template <typename KeyOf>
+  __device__ static uint32_t lane_offset(int i, int lane, uint32_t row_stride, KeyOf key_of) {
+    const int n = i * 64 + lane, r = n / CS, pos = n - r * CS;
+    return (uint32_t)key_of(r) * row_stride + 16u * (uint32_t)(pos < CD ? pos : 0);
+  }
+  template <typename KeyOf>
+  __device__ void init(uint32_t row_stride, int wave_, int lane, KeyOf key_of) {
+    wave = wave_;
+#pragma unroll
+    for (int u = 0; u < kFull; ++u) off[u] = lane_offset(wave + NW * u, lane, row_stride, key_of);
+    rem_inst = -1;
+    if constexpr (kRem != 0) {
+      const int rw = (wave + ROT) % NW;
+      rem_inst = rw < kRem ? kFull * NW + rw : -1;
+      off[kFull] = lane_offset(rem_inst < 0 ? 0 : rem_inst, lane, row_stride, key_of);
+    }
+  }
+  // r: resource whose byte 0 is the tile's first key row and whose range ends
+  // with the sequence's last row
+  __device__ void issue(rsrc_t r, uint8_t* lds_tile) const {
+#pragma unroll
+    for (int u = 0; u < kFull; ++u) buf_load_lds16(r, off[u], lds_tile + (wave + NW * u) * 1024);
+    if constexpr (kRem != 0)
+      if (rem_inst >= 0) buf_load_lds16(r, off[kFull], lds_tile + rem_inst * 1024);
+  }
+};
+
+// Byte offset of buffer (t mod N) in a ring of N buffers of `bytes` each.
+// The index passes through an empty asm statement so that the compiler treats
+// it as an opaque scalar: otherwise it strength-reduces every LDS address
+// built from it into a register of its own.
+template <int N>
+__device__ inline int ring_offset(int t, int bytes) {
+  int i = t % N;
+  asm volatile("" : "+s"(i));
+  return i * bytes;
+}
+
 __device__ inline v4i ld_lds16(const uint8_t* p) { return *(const v4i*)p; }
 __device__ inline void st_lds16(uint8_t* p, v4i x) { *(v4i*)p = x; }
 

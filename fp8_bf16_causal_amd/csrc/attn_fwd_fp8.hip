@@ -28,8 +28,8 @@
 //
 // Tiling (gfx950-specific, not from the pages): a workgroup of 8 waves owns
 // 256 consecutive query rows of one head; each wave owns 32 rows. K and V
-// tiles of 128 keys are staged in LDS, double-buffered, and shared by the 8
-// waves.
+// tiles of 128 keys are staged in LDS, in three buffers each, and shared by
+// the 8 waves.
 //  * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (neutral scales): each
 //    lane then holds one query (l%32) and 64 of the tile's keys, so row maxima
 //    are in-lane plus one permlane32 swap.
@@ -68,7 +68,8 @@ struct Fp8Layout {
   static constexpr int kKHiTile = kHi ? kBK * kKHiStride : 0;
   static constexpr int kKTile = kKLoTile + kKHiTile;
   static constexpr int kVTile = kBK * kVStride;
-  static constexpr int kLoop = 2 * (kKTile + kVTile);
+  static constexpr int kStages = 3;                   // buffers per operand
+  static constexpr int kLoop = kStages * (kKTile + kVTile);
   static constexpr int kEpi = kWaves * kQW * kOStride;
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
 };
@@ -92,17 +93,23 @@ __device__ inline int vrow_fp8(int k) { return k ^ (((k >> 5) & 1) << 2); }
 // cores while the other computes probabilities, order enforced by the
 // instruction stream because the hardware does not track MFMA completion.]
 //
-// K/V staging: in slot 2t the group-1 waves issue direct-to-LDS loads of K_{t+1}
-// and V_t into the buffers last read in slot 2t-1, and wait for them before
-// the barrier that closes slot 2t+1 (two slots of latency cover). K_t is read
-// in slots 2t and 2t+1, V_t in slots 2t+2 and 2t+3, so two buffers of each
-// suffice.
+// Within X_t the operand fragments are read from LDS two MFMA steps ahead in
+// one ring that runs from the P V steps into the Q K steps; the first two V
+// fragments are read at the end of Y_{t-1}, so the matrix cores start at the
+// barrier.
+//
+// K/V staging (three buffers per operand): in slot 2t the group-1 waves issue
+// direct-to-LDS loads of K_{t+2} and V_{t+1} and wait for them before the
+// barrier that closes slot 2t+1. V_t is read from slot 2t+1 (prefetch at the
+// end of group 0's Y_t) to slot 2t+3, K_t in slots 2t and 2t+1, so the buffer
+// a load overwrites was last read in the slot before, and a tile is first
+// read one slot after the barrier that publishes it.
 template <int DQK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p) {
   using L = Fp8Layout<DQK>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::kLds];
-  uint8_t* const Kbuf = lds;                    // 2 x kKTile
-  uint8_t* const Vbuf = lds + 2 * L::kKTile;    // 2 x kVTile
+  uint8_t* const Kbuf = lds;                            // kStages x kKTile
+  uint8_t* const Vbuf = lds + L::kStages * L::kKTile;   // kStages x kVTile
 
   // the wave index is wave-uniform: keep it (and all phase control) in scalar registers
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -140,19 +147,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
 
   // Only group 1 issues the direct-to-LDS loads, at the start of its softmax
   // phase (slot 2t), so that no wave starts a matrix phase behind a burst of
-  // its own memory instructions.
+  // its own memory instructions. Each tile goes through a buffer resource
+  // that starts at its first key and ends with key S - 1: rows past the
+  // sequence arrive as zeros (finite values whose keys every stored query
+  // masks).
   constexpr int kLoadWaves = kWaves / 2;
   const int lw = wave - kLoadWaves;
-  auto identity = [](int r) { return r; };
+  TileLoader<L::kBK, 9, 8, kLoadWaves, 0> kld;
+  TileLoader<L::kBK, 5, 4, kLoadWaves, 0> khld;
+  TileLoader<L::kBK, 9, 8, kLoadWaves, 2> vld;
+  if (grp == 1) {
+    auto identity = [](int r) { return r; };
+    kld.init(k_rs, lw, lane, identity);
+    if constexpr (L::kHi) khld.init(k_rs, lw, lane, identity);
+    vld.init(v_rs, lw, lane, vrow_fp8);
+  }
   auto issue_k = [&](int t) {
-    uint8_t* Kl = Kbuf + (t & 1) * L::kKTile;
-    load_tile_lds<L::kBK, 9, 8, kLoadWaves>(Kg, k_rs, t * L::kBK, S, Kl, lw, lane, identity);
-    if constexpr (L::kHi)
-      load_tile_lds<L::kBK, 5, 4, kLoadWaves>(Kg + 128, k_rs, t * L::kBK, S, Kl + L::kKLoTile, lw, lane, identity);
+    uint8_t* Kl = Kbuf + ring_offset<L::kStages>(t, L::kKTile);
+    const int k0 = t * L::kBK;
+    const uint8_t* src = Kg + (size_t)k0 * k_rs;
+    const uint32_t bytes = (uint32_t)(S - k0) * k_rs;  // through the end of key row S - 1's slot
+    kld.issue(make_rsrc(src, bytes), Kl);
+    if constexpr (L::kHi) khld.issue(make_rsrc(src + 128, bytes - 128), Kl + L::kKLoTile);
   };
   auto issue_v = [&](int t) {
-    uint8_t* Vl = Vbuf + (t & 1) * L::kVTile;
-    load_tile_lds<L::kBK, 9, 8, kLoadWaves>(Vg, v_rs, t * L::kBK, S, Vl, lw, lane, vrow_fp8);
+    uint8_t* Vl = Vbuf + ring_offset<L::kStages>(t, L::kVTile);
+    const int k0 = t * L::kBK;
+    vld.issue(make_rsrc(Vg + (size_t)k0 * v_rs, (uint32_t)(S - k0) * v_rs), Vl);
   };
 
   // Per-lane LDS offsets of the four ds_read_b64_tr_b8 reads that build the
@@ -172,6 +193,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   const int krd = l32 * L::kKLoStride + 16 * g;
   const int khrd = l32 * L::kKHiStride + 16 * g;
 
+  auto read_v = [&](const uint8_t* Vl, int db) {
+    const v2i r0 = lds_read_tr8(Vl + vrd[0] + 16 * db);
+    const v2i r1 = lds_read_tr8(Vl + vrd[1] + 16 * db);
+    const v2i r2 = lds_read_tr8(Vl + vrd[2] + 16 * db);
+    const v2i r3 = lds_read_tr8(Vl + vrd[3] + 16 * db);
+    return (v8i){r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
+  };
+  // QK step i = t6 * 4 + sb: K rows sb*32 + l32, bytes 64 t6 + 16 g and +32
+  auto read_k = [&](const uint8_t* Kl, int i) {
+    const int sb = i & 3, t6 = i >> 2;
+    const uint8_t* kp = t6 < 2 ? Kl + sb * 32 * L::kKLoStride + krd + 64 * t6
+                               : Kl + L::kKLoTile + sb * 32 * L::kKHiStride + khrd;
+    const v4i lo = ld_lds16(kp), hi = ld_lds16(kp + 32);
+    return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+
   v4f oacc[8][2];
   v4f lacc[2];
 #pragma unroll
@@ -182,48 +219,38 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
 
   v16f s[4];     // S_t^T, from X_t to Y_t
   v8i P[2];      // P_t codes in the 16x16x128 B layout, from Y_t to X_{t+1}
+  v8i vpre[2];   // V_t fragments of d-blocks 0 and 1, from the end of Y_t to X_{t+1}
   int sc0 = 127, sc1 = 127;
 #pragma unroll
-  for (int q = 0; q < 2; ++q) P[q] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+  for (int q = 0; q < 2; ++q) P[q] = vpre[q] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
 
   // X_t: the matrix phase of tile t (P V of tile t-1, then Q K^T of tile t).
   auto phase_x = [&](int tt) {
     // ================= X_tt: matrix phase
-    // Operand fragments are read two steps ahead of the MFMAs that use them;
-    // scheduling barriers keep the compiler from hoisting every LDS read of
-    // the phase to its top.
+    // One operand ring, two MFMA steps deep, runs through the P V steps into
+    // the Q K steps; scheduling barriers keep the compiler from hoisting
+    // every LDS read of the phase to its top.
     __builtin_amdgcn_s_setprio(1);
     const bool do_pv = tt >= 1 && tt - 1 < wave_tiles;
     const bool do_qk = tt < wave_tiles;
-    const uint8_t* Kl = Kbuf + (tt & 1) * L::kKTile;
-    const uint8_t* Vl = Vbuf + ((tt - 1) & 1) * L::kVTile;
-    auto read_v = [&](int db) {
-      const v2i r0 = lds_read_tr8(Vl + vrd[0] + 16 * db);
-      const v2i r1 = lds_read_tr8(Vl + vrd[1] + 16 * db);
-      const v2i r2 = lds_read_tr8(Vl + vrd[2] + 16 * db);
-      const v2i r3 = lds_read_tr8(Vl + vrd[3] + 16 * db);
-      return (v8i){r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
-    };
-    // QK step i = t6 * 4 + sb: K rows sb*32 + l32, bytes 64 t6 + 16 g and +32
-    auto read_k = [&](int i) {
-      const int sb = i & 3, t6 = i >> 2;
-      const uint8_t* kp = t6 < 2 ? Kl + sb * 32 * L::kKLoStride + krd + 64 * t6
-                                 : Kl + L::kKLoTile + sb * 32 * L::kKHiStride + khrd;
-      const v4i lo = ld_lds16(kp), hi = ld_lds16(kp + 32);
-      return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    };
+    const uint8_t* Kl = Kbuf + ring_offset<L::kStages>(tt, L::kKTile);
+    const uint8_t* Vl = Vbuf + ring_offset<L::kStages>(tt + L::kStages - 1, L::kVTile);
     constexpr int kQkSteps = 4 * (DQK / 64);
     // S_{tt-1} was consumed by Y_{tt-1}: end its live range here (an empty
     // asm definition, no instruction) so it does not occupy registers
     // through the P V half of this phase.
     asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
+    v8i kf[3];
     if (do_pv) {
       v8i vf[3];
-      vf[0] = read_v(0);
-      vf[1] = read_v(1);
+      vf[0] = vpre[0];
+      vf[1] = vpre[1];
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        if (db + 2 < 8) vf[(db + 2) % 3] = read_v(db + 2);
+        if (db + 2 < 8)
+          vf[(db + 2) % 3] = read_v(Vl, db + 2);
+        else
+          kf[db - 6] = read_k(Kl, db - 6);  // the first two Q K steps
         oacc[db][0] = mfma_16x16x128_fp8(vf[db % 3], P[0], oacc[db][0], 127, sc0);
         oacc[db][1] = mfma_16x16x128_fp8(vf[db % 3], P[1], oacc[db][1], 127, sc1);
         __builtin_amdgcn_sched_barrier(0);
@@ -233,14 +260,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       lacc[0] = mfma_16x16x128_fp8(ones, P[0], lacc[0], 127, sc0);
       lacc[1] = mfma_16x16x128_fp8(ones, P[1], lacc[1], 127, sc1);
       __builtin_amdgcn_sched_barrier(0);
+    } else {
+      kf[0] = read_k(Kl, 0);
+      kf[1] = read_k(Kl, 1);
     }
     if (do_qk) {
-      v8i kf[3];
-      kf[0] = read_k(0);
-      kf[1] = read_k(1);
 #pragma unroll
       for (int i = 0; i < kQkSteps; ++i) {
-        if (i + 2 < kQkSteps) kf[(i + 2) % 3] = read_k(i + 2);
+        if (i + 2 < kQkSteps) kf[(i + 2) % 3] = read_k(Kl, i + 2);
         s[i & 3] = mfma_32x32x64_fp8(kf[i % 3], qf[i >> 2], i < 4 ? (v16f){} : s[i & 3], 127, 127);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -335,9 +362,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       lacc[0] *= a0;
       lacc[1] *= a1;
     }
+    // the first two V fragments of X_{tt+1} (V_tt is resident: see above)
+    const uint8_t* Vn = Vbuf + ring_offset<L::kStages>(tt, L::kVTile);
+    vpre[0] = read_v(Vn, 0);
+    vpre[1] = read_v(Vn, 1);
   };
 
-  if (grp == 1) issue_k(0);
+  if (grp == 1) {
+    issue_k(0);
+    if (n_tiles > 1) issue_k(1);
+    issue_v(0);
+  }
   wait_vmem();
   lds_barrier();
 
@@ -354,14 +389,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      if (t < n_tiles) {                       // slot 2t: Y_{t-1}
-        if (t + 1 < n_tiles) issue_k(t + 1);
-        issue_v(t);
-      }
+      if (t + 2 < n_tiles) issue_k(t + 2);     // slot 2t: Y_{t-1}
+      if (t + 1 < n_tiles) issue_v(t + 1);
       if (t >= 1 && t - 1 < wave_tiles) phase_y(t - 1);
       lds_barrier();
       phase_x(t);                              // slot 2t + 1: X_t
-      if (t < n_tiles) wait_vmem();            // slot 2t's loads are first read in slot 2t + 2
+      wait_vmem();                             // slot 2t's loads are first read in slot 2t + 3
       lds_barrier();
     }
   }
