@@ -221,9 +221,14 @@ struct TileLoader {
   // with the sequence's last row
   __device__ void issue(rsrc_t r, uint8_t* lds_tile) const {
 #pragma unroll
-    for (int u = 0; u < kFull; ++u) buf_load_lds16(r, off[u], lds_tile + (wave + NW * u) * 1024);
-    if constexpr (kRem != 0)
-      if (rem_inst >= 0) buf_load_lds16(r, off[kFull], lds_tile + rem_inst * 1024);
+    for (int u = 0; u < kRegs; ++u) issue_one(r, lds_tile, u);
+  }
+  // instruction u (0 .. kRegs-1) of this wave's share; u must be a constant
+  __device__ void issue_one(rsrc_t r, uint8_t* lds_tile, int u) const {
+    if (u < kFull)
+      buf_load_lds16(r, off[u], lds_tile + (wave + NW * u) * 1024);
+    else if (rem_inst >= 0)
+      buf_load_lds16(r, off[kFull], lds_tile + rem_inst * 1024);
   }
 };
 

@@ -33,18 +33,19 @@
 //  * S^T = K Q^T on v_mfma_scale_f32_32x32x64_f8f6f4 (neutral scales): each
 //    lane then holds one query (l%32) and 64 of the tile's keys, so row maxima
 //    are in-lane plus one permlane32 swap.
-//  * The P codes are regrouped with permlane16 swaps into the operand layout
-//    of v_mfma_scale_f32_16x16x128_f8f6f4, which computes O^T = V^T P^T in
-//    16x16 blocks: K = 128 keys per instruction, bytes 0-15 of every lane in
-//    the first 64-key scale block and bytes 16-31 in the second, so each
-//    lane's scale byte is 127 - k of its query and block.
+//  * The P codes go straight into the B operand of the same 32x32x64
+//    instruction computing O^T = V^T P^T: a lane's 16 scores of one 32-key
+//    block become 16 code bytes in accumulator order, two blocks (one 64-key
+//    scale block) per instruction, so each lane's scale byte is 127 - k of
+//    its own query and block. The V^T operand is read from LDS in the
+//    matching key order (ds_read_b64_tr_b8).
 //  * The same P operand against an all-ones A operand gives the rounded row
-//    sum: one 16x16x128 instruction per 16 queries and 128 keys, 1/16 of the
-//    P V work (the pages' +6 percent).
+//    sum: one more 32x32x64 instruction per 64-key block (a 16x16x128 one
+//    would mix the scales of two queries in one K block).
 //  * K and V are copied global -> LDS by direct-to-LDS loads (no staging
 //    registers) into padded row-major tiles; V's rows are permuted so that
-//    the transposing reads (ds_read_b64_tr_b8) building the V^T operand are
-//    free of bank conflicts.
+//    the transposing reads building the V^T operand are free of bank
+//    conflicts.
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -74,17 +75,26 @@ struct Fp8Layout {
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
 };
 
-// V's LDS row for key k of the tile: within each 64-key half, keys 32..63
-// trade places in groups of four (bit 2 flips when bit 5 is set). One
-// ds_read_b64_tr_b8 pass serves two 16-lane groups whose keys are 32 apart;
-// with the 144-byte stride their 16 rows then fall in 16 distinct bank groups.
-__device__ inline int vrow_fp8(int k) { return k ^ (((k >> 5) & 1) << 2); }
+// V's LDS row for key k of the tile: the low four bits b3 b2 b1 b0 of k
+// become b3 b1 b0 b2. One ds_read_b64_tr_b8 pass (32 lanes) reads the eight
+// keys {0-3, 8-11} or {4-7, 12-15} of a 16-key group, 32 bytes each; they
+// land on the eight even or the eight odd rows of the group, whose 144-byte
+// strides put them in eight distinct groups of 8 banks.
+__device__ inline int vrow_fp8(int k) {
+  const int x = k & 15;
+  return (k & ~15) | ((x >> 3) & 1) << 3 | (x & 3) << 1 | ((x >> 2) & 1);
+}
+// the key held by V's LDS row r (inverse of vrow_fp8)
+__device__ inline int vkey_fp8(int r) {
+  const int n = r & 15;
+  return (r & ~15) | ((n >> 3) & 1) << 3 | (n & 1) << 2 | (n >> 1) & 3;
+}
 
 // Ping-pong schedule. The workgroup's 8 waves form two groups (waves w and
 // w + 4 share a SIMD). Time is cut into slots separated by workgroup
 // barriers; in slot p group 0 runs its phase p and group 1 its phase p - 1.
 // A wave's phases alternate
-//   X_t: O^T += V^T P_{t-1}^T (and the row-sum MFMA), then S_t^T = K_t Q^T   [matrix cores]
+//   X_t: O^T += V^T P_{t-1}^T (and the row-sum MFMAs), then S_t^T = K_t Q^T  [matrix cores]
 //   Y_t: softmax of S_t: maxima, block exponents, Lean P codes, rescale       [vector ALU]
 // so on every SIMD one wave issues matrix instructions while its partner
 // computes probabilities, and they swap at the next barrier.
@@ -98,12 +108,16 @@ __device__ inline int vrow_fp8(int k) { return k ^ (((k >> 5) & 1) << 2); }
 // fragments are read at the end of Y_{t-1}, so the matrix cores start at the
 // barrier.
 //
-// K/V staging (three buffers per operand): in slot 2t the group-1 waves issue
-// direct-to-LDS loads of K_{t+2} and V_{t+1} and wait for them before the
-// barrier that closes slot 2t+1. V_t is read from slot 2t+1 (prefetch at the
-// end of group 0's Y_t) to slot 2t+3, K_t in slots 2t and 2t+1, so the buffer
-// a load overwrites was last read in the slot before, and a tile is first
-// read one slot after the barrier that publishes it.
+// K/V staging (three buffers per operand): each group copies one operand,
+// from its softmax phases, one direct-to-LDS instruction at a time spread
+// through the code generation (a burst at the start of the phase would hold
+// up its vector instructions behind the memory instructions). Group 1 loads
+// V_{t+1} during Y_{t-1} (slot 2t) and waits for it at the end of X_t (slot
+// 2t+1); group 0 loads K_{t+2} during Y_t (slot 2t+1) and waits at the end of
+// X_{t+1} (slot 2t+2). K_t is read in slots 2t and 2t+1, V_t from slot 2t+1
+// (prefetch at the end of group 0's Y_t) to slot 2t+3: each load overwrites a
+// buffer last read at least one slot before it starts, and each tile is
+// published at least one slot before it is first read.
 template <int DQK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p) {
   using L = Fp8Layout<DQK>;
@@ -145,59 +159,57 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     }
   }
 
-  // Only group 1 issues the direct-to-LDS loads, at the start of its softmax
-  // phase (slot 2t), so that no wave starts a matrix phase behind a burst of
-  // its own memory instructions. Each tile goes through a buffer resource
-  // that starts at its first key and ends with key S - 1: rows past the
-  // sequence arrive as zeros (finite values whose keys every stored query
-  // masks).
-  constexpr int kLoadWaves = kWaves / 2;
-  const int lw = wave - kLoadWaves;
-  TileLoader<L::kBK, 9, 8, kLoadWaves, 0> kld;
-  TileLoader<L::kBK, 5, 4, kLoadWaves, 0> khld;
-  TileLoader<L::kBK, 9, 8, kLoadWaves, 2> vld;
-  if (grp == 1) {
-    auto identity = [](int r) { return r; };
-    kld.init(k_rs, lw, lane, identity);
-    if constexpr (L::kHi) khld.init(k_rs, lw, lane, identity);
-    vld.init(v_rs, lw, lane, vrow_fp8);
-  }
-  auto issue_k = [&](int t) {
+  // Each tile goes through a buffer resource that starts at its first key and
+  // ends with key S - 1: rows past the sequence arrive as zeros (finite
+  // values whose keys every stored query masks). Group 0 (waves 0-3) copies K
+  // tiles, group 1 (waves 4-7) V tiles.
+  constexpr int kGroupWaves = kWaves / 2;
+  const int gw = wave & (kGroupWaves - 1);
+  TileLoader<L::kBK, 9, 8, kGroupWaves, 0> kld;
+  TileLoader<L::kBK, 5, 4, kGroupWaves, 2> khld;
+  TileLoader<L::kBK, 9, 8, kGroupWaves, 0> vld;
+  constexpr int kKLoads = decltype(kld)::kRegs + (L::kHi ? decltype(khld)::kRegs : 0);
+  constexpr int kVLoads = decltype(vld)::kRegs;
+  // load u of this wave's share of K tile t (u = 0 .. kKLoads-1)
+  auto load_k = [&](int t, int u) {
     uint8_t* Kl = Kbuf + ring_offset<L::kStages>(t, L::kKTile);
     const int k0 = t * L::kBK;
     const uint8_t* src = Kg + (size_t)k0 * k_rs;
     const uint32_t bytes = (uint32_t)(S - k0) * k_rs;  // through the end of key row S - 1's slot
-    kld.issue(make_rsrc(src, bytes), Kl);
-    if constexpr (L::kHi) khld.issue(make_rsrc(src + 128, bytes - 128), Kl + L::kKLoTile);
+    if (u < decltype(kld)::kRegs)
+      kld.issue_one(make_rsrc(src, bytes), Kl, u);
+    else if constexpr (L::kHi)
+      khld.issue_one(make_rsrc(src + 128, bytes - 128), Kl + L::kKLoTile, u - decltype(kld)::kRegs);
   };
-  auto issue_v = [&](int t) {
+  auto load_v = [&](int t, int u) {
     uint8_t* Vl = Vbuf + ring_offset<L::kStages>(t, L::kVTile);
     const int k0 = t * L::kBK;
-    vld.issue(make_rsrc(Vg + (size_t)k0 * v_rs, (uint32_t)(S - k0) * v_rs), Vl);
+    vld.issue_one(make_rsrc(Vg + (size_t)k0 * v_rs, (uint32_t)(S - k0) * v_rs), Vl, u);
   };
 
-  // Per-lane LDS offsets of the four ds_read_b64_tr_b8 reads that build the
-  // V^T operand of one 16x16x128 instruction (d-block 0; d-block db adds
-  // 16 db). Read j covers operand bytes 8j .. 8j+7; its 8 rows are the keys
-  // whose P codes sit in those bytes of the P operand.
-  int vrd[4];
+  // V^T operand of O^T = V^T P^T (32x32x64): A lane (dv row i, half g) byte
+  // 16 h + 4 e + x pairs with the P code of key 32 (2 ks + h) + 8 e + 4 g + x
+  // (the key the S^T accumulator of lane (., g) holds in register 4 e + x).
+  // Read j (bytes 8j .. 8j+7) covers keys 16 j + 64 ks + {8 e' + 4 g + x}: in
+  // each 16-lane group, lanes 2k and 2k+1 address the two 8-byte halves of
+  // the 16 dv columns of the k-th of those keys. d-block dvb adds 32 dvb.
+  int vrd;
   {
-    const int g16 = lane >> 4, pp = lane & 15, bb = pp >> 1, hh = pp & 1;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = 64 * (j >> 1) + 32 * (g16 & 1) + 4 * (g16 >> 1) + 16 * (j & 1) + 8 * (bb >> 2) + (bb & 3);
-      vrd[j] = vrow_fp8(key) * L::kVStride + 8 * hh;
-    }
+    const int G = lane >> 4, cc = lane & 15, k = cc >> 1;
+    const int key = 8 * (k >> 2) + 4 * (G >> 1) + (k & 3);
+    vrd = vrow_fp8(key) * L::kVStride + 16 * (G & 1) + 8 * (cc & 1);
   }
   // K operand: block sb reads row sb*32 + l32, chunks 4 t6 + g and 4 t6 + 2 + g
   const int krd = l32 * L::kKLoStride + 16 * g;
   const int khrd = l32 * L::kKHiStride + 16 * g;
 
-  auto read_v = [&](const uint8_t* Vl, int db) {
-    const v2i r0 = lds_read_tr8(Vl + vrd[0] + 16 * db);
-    const v2i r1 = lds_read_tr8(Vl + vrd[1] + 16 * db);
-    const v2i r2 = lds_read_tr8(Vl + vrd[2] + 16 * db);
-    const v2i r3 = lds_read_tr8(Vl + vrd[3] + 16 * db);
+  // PV step i = 4 ks + dvb
+  auto read_v = [&](const uint8_t* Vl, int i) {
+    const uint8_t* vp = Vl + vrd + 64 * (i >> 2) * L::kVStride + 32 * (i & 3);
+    const v2i r0 = lds_read_tr8(vp);
+    const v2i r1 = lds_read_tr8(vp + 16 * L::kVStride);
+    const v2i r2 = lds_read_tr8(vp + 32 * L::kVStride);
+    const v2i r3 = lds_read_tr8(vp + 48 * L::kVStride);
     return (v8i){r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
   };
   // QK step i = t6 * 4 + sb: K rows sb*32 + l32, bytes 64 t6 + 16 g and +32
@@ -209,18 +221,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
 
-  v4f oacc[8][2];
-  v4f lacc[2];
+  // O^T in four 32x32 blocks (lane (query l32, g), register r: dv row
+  // 32 dvb + 8 (r/4) + 4 g + r%4); every register of lacc holds the query's
+  // rounded row sum.
+  v16f oacc[4];
+  v16f lacc;
 #pragma unroll
-  for (int db = 0; db < 8; ++db) oacc[db][0] = oacc[db][1] = (v4f){0.f, 0.f, 0.f, 0.f};
-  lacc[0] = lacc[1] = (v4f){0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < 4; ++d) oacc[d] = (v16f){};
+  lacc = (v16f){};
   float m = -INFINITY;  // running max of the raw scores of query qw0 + l32
   const float c = p.c, c8 = 8.0f * p.c;
 
   v16f s[4];     // S_t^T, from X_t to Y_t
-  v8i P[2];      // P_t codes in the 16x16x128 B layout, from Y_t to X_{t+1}
-  v8i vpre[2];   // V_t fragments of d-blocks 0 and 1, from the end of Y_t to X_{t+1}
-  int sc0 = 127, sc1 = 127;
+  v8i P[2];      // P_t codes (64-key block ks in P[ks]), from Y_t to X_{t+1}
+  v8i vpre[2];   // V_t fragments of PV steps 0 and 1, from the end of Y_t to X_{t+1}
+  int sc[2] = {127, 127};  // E8M0 scale bytes of P[0], P[1]: 127 - k
 #pragma unroll
   for (int q = 0; q < 2; ++q) P[q] = vpre[q] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
 
@@ -242,24 +257,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
     v8i kf[3];
     if (do_pv) {
+      const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
       v8i vf[3];
       vf[0] = vpre[0];
       vf[1] = vpre[1];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        if (db + 2 < 8)
-          vf[(db + 2) % 3] = read_v(Vl, db + 2);
+      for (int i = 0; i < 8; ++i) {
+        const int ks = i >> 2, dvb = i & 3;
+        if (i + 2 < 8)
+          vf[(i + 2) % 3] = read_v(Vl, i + 2);
         else
-          kf[db - 6] = read_k(Kl, db - 6);  // the first two Q K steps
-        oacc[db][0] = mfma_16x16x128_fp8(vf[db % 3], P[0], oacc[db][0], 127, sc0);
-        oacc[db][1] = mfma_16x16x128_fp8(vf[db % 3], P[1], oacc[db][1], 127, sc1);
+          kf[i - 6] = read_k(Kl, i - 6);  // the first two Q K steps
+        oacc[dvb] = mfma_32x32x64_fp8(vf[i % 3], P[ks], oacc[dvb], 127, sc[ks]);
         __builtin_amdgcn_sched_barrier(0);
+        if (dvb == 3) {
+          lacc = mfma_32x32x64_fp8(ones, P[ks], lacc, 127, sc[ks]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                        0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
-      lacc[0] = mfma_16x16x128_fp8(ones, P[0], lacc[0], 127, sc0);
-      lacc[1] = mfma_16x16x128_fp8(ones, P[1], lacc[1], 127, sc1);
-      __builtin_amdgcn_sched_barrier(0);
     } else {
       kf[0] = read_k(Kl, 0);
       kf[1] = read_k(Kl, 1);
@@ -274,8 +290,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     }
     __builtin_amdgcn_s_setprio(0);
   };
-  // Y_t: the softmax phase of tile t.
-  auto phase_y = [&](int tt) {
+  // Y_t: the softmax phase of tile t. ld(u), u = 0..7, issues this wave's
+  // u-th tile load of the slot (or nothing); the calls are spread through the
+  // code generation.
+  auto phase_y = [&](int tt, auto&& ld) {
     // ================= Y_tt: softmax phase
     const int k0 = tt * L::kBK;
     if (k0 + L::kBK - 1 > qw0) {  // the tile crosses this wave's diagonal
@@ -316,62 +334,59 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     const float kb = fminf(fmaxf(floorf(8.0f - (mb - mn) * c), 0.0f), 127.0f);
     const float bias_a = fmaf(-c8, mn, kLeanPC + 8.0f * ka);
     const float bias_b = fmaf(-c8, mn, kLeanPC + 8.0f * kb);
-    // Lean P: code = u8(8 c s + C + 8k - 8 c m), four codes per dword
-    uint32_t X[4][4];
+    // Lean P: code = u8(8 c s + C + 8k - 8 c m), four codes per dword, in
+    // accumulator order: P[ks] dword d holds registers 4(d%4) .. +3 of
+    // s[2 ks + d/4]
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      const float bias = sb < 2 ? bias_a : bias_b;
+    for (int ks = 0; ks < 2; ++ks) {
+      const float bias = ks == 0 ? bias_a : bias_b;
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
+      for (int d = 0; d < 8; ++d) {
+        const v16f& sv = s[2 * ks + (d >> 2)];
+        const int r0 = 4 * (d & 3);
         uint32_t w = 0;
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 0], c8, bias), 0, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 1], c8, bias), 1, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 2], c8, bias), 2, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(s[sb][4 * v + 3], c8, bias), 3, w);
-        X[sb][v] = w;
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 0], c8, bias), 0, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 1], c8, bias), 1, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 2], c8, bias), 2, w);
+        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 3], c8, bias), 3, w);
+        P[ks][d] = (int)w;
+        if (d & 1) ld(4 * ks + (d >> 1));
       }
     }
-    // regroup into the 16x16x128 B-operand layout: P[Q] serves queries
-    // qw0 + 16Q .. +15; bytes 0-15 = keys 0..63, bytes 16-31 = keys 64..127
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      auto pa = __builtin_amdgcn_permlane16_swap(X[0][v], X[1][v], false, false);
-      auto pb = __builtin_amdgcn_permlane16_swap(X[2][v], X[3][v], false, false);
-      P[0][v] = (int)pa[0];
-      P[1][v] = (int)pa[1];
-      P[0][4 + v] = (int)pb[0];
-      P[1][4 + v] = (int)pb[1];
-    }
-    // E8M0 scale of P: lane i + 16*kb carries (query i of the block,
-    // 32-key group kb); groups 0-1 are the first 64-key block, 2-3 the second
-    const uint32_t scu = (uint32_t)(127 - (int)(lane < 32 ? ka : kb));
-    auto scp = __builtin_amdgcn_permlane16_swap(scu, scu, false, false);
-    sc0 = (int)scp[0];
-    sc1 = (int)scp[1];
+    sc[0] = 127 - (int)ka;
+    sc[1] = 127 - (int)kb;
     // rescale the accumulators when the running max rose
-    auto ap = __builtin_amdgcn_permlane16_swap(as_u(alpha), as_u(alpha), false, false);
-    const float a0 = as_f(ap[0]), a1 = as_f(ap[1]);
     if (__any(alpha != 1.0f)) {
       // keep this a real branch: the multiplies are skipped on most tiles
       asm volatile("" ::: "memory");
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        oacc[db][0] *= a0;
-        oacc[db][1] *= a1;
-      }
-      lacc[0] *= a0;
-      lacc[1] *= a1;
+      for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
+      lacc *= alpha;
     }
-    // the first two V fragments of X_{tt+1} (V_tt is resident: see above)
+    // the first two V fragments of X_{tt+1} (V_tt is resident: see above),
+    // read after the codes so that S and the fragments are never live together
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* Vn = Vbuf + ring_offset<L::kStages>(tt, L::kVTile);
     vpre[0] = read_v(Vn, 0);
     vpre[1] = read_v(Vn, 1);
   };
 
-  if (grp == 1) {
-    issue_k(0);
-    if (n_tiles > 1) issue_k(1);
-    issue_v(0);
+  if (grp == 0) {
+    auto identity = [](int r) { return r; };
+    kld.init(k_rs, gw, lane, identity);
+    if constexpr (L::kHi) khld.init(k_rs, gw, lane, identity);
+#pragma unroll
+    for (int u = 0; u < kKLoads; ++u) {
+      load_k(0, u);
+      if (n_tiles > 1) load_k(1, u);
+    }
+  } else {
+    vld.init(v_rs, gw, lane, vkey_fp8);
+#pragma unroll
+    for (int u = 0; u < kVLoads; ++u) {
+      load_v(0, u);
+      if (n_tiles > 1) load_v(1, u);
+    }
   }
   wait_vmem();
   lds_barrier();
@@ -379,42 +394,51 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // Each group runs its own copy of the slot loop (2 slots per iteration), so
   // that S never has to stay live across the loop's back edge in group 0 and
   // P never in group 1. Both copies execute the same barriers in the same
-  // slots; group 1 also stages the tiles.
+  // slots. Every wave runs a softmax phase in every slot of the workgroup's
+  // tile range, also past its own diagonal (all keys masked there) or with
+  // all of its rows past S (never stored): the phase carries the group's
+  // tile loads, and the probabilities it makes are never used.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
       phase_x(t);                              // slot 2t: X_t
+      wait_vmem();                             // K_{t+1}, loaded in slot 2t-1
       lds_barrier();
-      if (t < wave_tiles) phase_y(t);          // slot 2t + 1: Y_t
+      if (t < n_tiles) {                       // slot 2t + 1: Y_t, loads K_{t+2}
+        const bool ldk = t + 2 < n_tiles;
+        phase_y(t, [&](int u) {
+          if (u < kKLoads && ldk) load_k(t + 2, u);
+        });
+      }
       lds_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      if (t + 2 < n_tiles) issue_k(t + 2);     // slot 2t: Y_{t-1}
-      if (t + 1 < n_tiles) issue_v(t + 1);
-      if (t >= 1 && t - 1 < wave_tiles) phase_y(t - 1);
+      if (t >= 1) {                            // slot 2t: Y_{t-1}, loads V_{t+1}
+        const bool ldv = t + 1 < n_tiles;
+        phase_y(t - 1, [&](int u) {
+          if (u < kVLoads && ldv) load_v(t + 1, u);
+        });
+      }
       lds_barrier();
       phase_x(t);                              // slot 2t + 1: X_t
-      wait_vmem();                             // slot 2t's loads are first read in slot 2t + 3
+      wait_vmem();                             // V_{t+1}, loaded in slot 2t
       lds_barrier();
     }
   }
 
   // ---- epilogue: O / l * dv -> BF16, staged through LDS for coalesced rows.
-  // oacc[db][Q] lane (c16, g16) register r: query qw0 + 16Q + c16, column
-  // 16 db + 4 g16 + r; lacc[Q] holds that query's rounded sum in every register.
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
-    const int c16 = lane & 15, g16 = lane >> 4;
+    const float inv = p.dv / lacc[0];
 #pragma unroll
-    for (int Q = 0; Q < 2; ++Q) {
-      const float inv = p.dv / lacc[Q][0];
+    for (int d = 0; d < 4; ++d)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const v4f o = oacc[db][Q] * inv;
-        const v2i w = {(int)pack_bf16(o[0], o[1]), (int)pack_bf16(o[2], o[3])};
-        *(v2i*)(Ol + (16 * Q + c16) * kOStride + (16 * db + 4 * g16) * 2) = w;
+      for (int e = 0; e < 4; ++e) {
+        const int col = 32 * d + 8 * e + 4 * g;
+        const v2i w = {(int)pack_bf16(oacc[d][4 * e] * inv, oacc[d][4 * e + 1] * inv),
+                       (int)pack_bf16(oacc[d][4 * e + 2] * inv, oacc[d][4 * e + 3] * inv)};
+        *(v2i*)(Ol + l32 * kOStride + col * 2) = w;
       }
-    }
   }
   __syncthreads();
   if (wave_tiles > 0) {
