@@ -30,6 +30,44 @@ PATHS = ["fp8_mha_s32k", "bf16_mha_s32k"]
 PAGES_TFLOPS = {"fp8_mha_s32k": 2672.0}  # the pages' own FP8 figure on this workload (context)
 
 
+# Sources whose text defines each kernel's code and launch: a stored HBM
+# traffic figure is used only while their hash matches the one recorded with it.
+KERNEL_SOURCES = {
+    "fp8": ["fp8_bf16_causal_amd/csrc/attn_common.h", "fp8_bf16_causal_amd/csrc/attn_api.cpp",
+            "fp8_bf16_causal_amd/csrc/attn_fwd_fp8.hip", "fp8_bf16_causal_amd/build.py"],
+    "bf16": ["fp8_bf16_causal_amd/csrc/attn_common.h", "fp8_bf16_causal_amd/csrc/attn_api.cpp",
+             "fp8_bf16_causal_amd/csrc/attn_fwd_bf16.hip", "fp8_bf16_causal_amd/build.py"],
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s32k_hbm_traffic.txt")
+
+
+def sources_sha256(kind):
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (copy-calibrated), or None if it is missing or was taken on
+    other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            lines = [ln.split() for ln in f if ln.startswith("workload=")]
+    except OSError:
+        return None
+    sha = sources_sha256(kind)
+    for fields in lines:
+        kv = dict(x.split("=", 1) for x in fields)
+        if kv.get("workload") == workload and kv.get("sources_sha256") == sha:
+            return int(kv["traffic_bytes"])
+    return None
+
+
 def causal_flops(p):
     return float(p["B"]) * p["Hq"] * p["S"] * p["S"] * (p["Dqk"] + p["Dv"])
 
@@ -68,7 +106,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=2048, help="rows per path in the CPU-baseline sample")
+    ap.add_argument("--cpu-rows", type=int, default=8192, help="rows per path in the CPU-baseline sample (about 10-15 s of oracle time)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known byte count for HBM counters)")
     ap.add_argument("--paths", default=",".join(PATHS))
@@ -147,7 +185,9 @@ def main():
     dom = max(names, key=lambda n: paths[n]["kernel_ms_avg"])
     dom_kind = inputs[dom].dtype
     roofline = {"bound": "mfma", "achieved": paths[dom]["tflops"], "peak": PEAK[dom_kind], "unit": "TFLOP/s",
-                "frac": paths[dom]["frac_of_peak"], "traffic": None, "kernel": dom}
+                "frac": paths[dom]["frac_of_peak"], "traffic": measured_traffic(dom, dom_kind), "kernel": dom}
+    for n in names:
+        paths[n]["hbm_traffic_bytes"] = measured_traffic(n, inputs[n].dtype)
     cfg = {"workload": "+".join(names), "B": 1, "H": 32, "S": 32768, "Dqk": 128, "Dv": 128,
            "input": "Gaussian N(0,1), seeds 3 (fp8) and 4 (bf16), per-tensor e4m3 scales",
            "flop_count": "causal B*H*S^2*(Dqk+Dv)"}
