@@ -39,6 +39,7 @@ KERNEL_SOURCES = {
              "fp8_bf16_causal_amd/csrc/attn_fwd_bf16.hip", "fp8_bf16_causal_amd/build.py"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s32k_hbm_traffic.txt")
+CLOCK_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s32k_mfma_clock_lds.txt")
 
 
 def sources_sha256(kind):
@@ -51,12 +52,11 @@ def sources_sha256(kind):
     return h.hexdigest()
 
 
-def measured_traffic(workload, kind):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary (copy-calibrated), or None if it is missing or was taken on
-    other kernel sources."""
+def profiled_line(path, workload, kind):
+    """The key=value fields of the line for `workload` in a committed profile
+    summary, if it was taken on the current kernel sources."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             lines = [ln.split() for ln in f if ln.startswith("workload=")]
     except OSError:
         return None
@@ -64,8 +64,16 @@ def measured_traffic(workload, kind):
     for fields in lines:
         kv = dict(x.split("=", 1) for x in fields)
         if kv.get("workload") == workload and kv.get("sources_sha256") == sha:
-            return int(kv["traffic_bytes"])
+            return kv
     return None
+
+
+def measured_traffic(workload, kind):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (copy-calibrated), or None if it is missing or was taken on
+    other kernel sources."""
+    kv = profiled_line(TRAFFIC_FILE, workload, kind)
+    return int(kv["traffic_bytes"]) if kv else None
 
 
 def causal_flops(p):
@@ -104,7 +112,7 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=400, help="untimed steps first (the default, about 5 s, lets the clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=8192, help="rows per path in the CPU-baseline sample (about 10-15 s of oracle time)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -158,7 +166,6 @@ def main():
             ev[n][s][1].record()
     stop.record()
     torch.cuda.synchronize()
-    sclk = None  # the sustained clock comes from rocprofv3 (GRBM_GUI_ACTIVE / kernel time)
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
@@ -172,11 +179,16 @@ def main():
         flop_step += f
         ideal_s += f / (PEAK[kind] * 1e12)
         tf = f / (avg * 1e-3) / 1e12
-        paths[n] = {"kernel_ms_avg": round(avg, 4), "kernel_ms_min": round(min(ms), 4),
+        med = sorted(ms)[len(ms) // 2]
+        paths[n] = {"kernel_ms_avg": round(avg, 4), "kernel_ms_median": round(med, 4), "kernel_ms_min": round(min(ms), 4),
                     "tflops": round(tf, 1), "tflops_literal_2x": round(2 * tf, 1),
                     "peak_tflops": PEAK[kind], "frac_of_peak": round(tf / PEAK[kind], 4)}
-        if sclk:
-            paths[n]["frac_of_peak_at_measured_clock"] = round(tf / (PEAK[kind] * sclk / 2400.0), 4)
+        ck = profiled_line(CLOCK_FILE, n, kind)
+        if ck:  # sustained clock of the same kernel in the committed rocprofv3 profile
+            mhz = float(ck["sclk_mhz"])
+            paths[n]["sclk_mhz_profiled"] = mhz
+            paths[n]["frac_of_peak_at_profiled_clock"] = round(tf / (PEAK[kind] * mhz / 2400.0), 4)
+            paths[n]["mfma_busy_profiled"] = float(ck["mfma_busy"])
         if n in PAGES_TFLOPS:
             paths[n]["pages_tflops"] = PAGES_TFLOPS[n]
             paths[n]["ratio_to_pages"] = round(tf / PAGES_TFLOPS[n], 3)
@@ -195,7 +207,7 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "+".join(sorted({inputs[n].dtype for n in names})), "data": "synthetic",
             "config": cfg, "frac_of_peak": round(ideal_s / (ms_per_step * 1e-3), 4),
-            "sclk_mhz_after_timing": sclk, "paths": paths, "roofline": roofline}
+            "paths": paths, "roofline": roofline}
     if not args.no_cpu_baseline:
         threads = min(int(os.environ.get("OMP_NUM_THREADS", "16")), os.cpu_count() or 1, 16)
         line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_rows, threads)

@@ -7,8 +7,8 @@
 // FlashAttention forward with an exact online softmax,
 //   S = Q K^T, m = running row max, P = 2^((S - m) c) rounded to BF16,
 //   O = sum P V / sum P, rescaled by 2^((m_old - m_new) c) when m rises.
-// Readings: the row sum accumulates the fp32 probabilities (before their BF16
-// rounding); the reference max is updated per key tile, lazily (only when the
+// Readings: the row sum accumulates the BF16-rounded probabilities (the
+// weights the P V product actually applies); the reference max is updated per key tile, lazily (only when the
 // tile max exceeds it by more than 8 binades), with an exact rescale then.
 //
 // Tiling (gfx950-specific): 8 waves x 32 query rows per workgroup; K/V tiles
@@ -19,6 +19,8 @@
 // the probabilities feed the P V instruction straight from registers. V stays
 // row-major in LDS (rows permuted); the V^T operand is read with
 // ds_read_b64_tr_b16.
+#include <type_traits>
+
 #include "attn_common.h"
 #include "attn_launch.h"
 
@@ -166,30 +168,42 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
     // S_{tt-1} was consumed by Y_{tt-1}: end its live range (no instruction)
 #pragma unroll
     for (int sb = 0; sb < L::kNsb; ++sb) asm volatile("" : "=v"(s[sb]));
-    // operand fragments are read two steps ahead of the MFMAs that use them
-    if (do_pv) {
-      v8bf vf[3];
-      vf[0] = read_v(0);
-      vf[1] = read_v(1);
-#pragma unroll
-      for (int i = 0; i < kPvSteps; ++i) {
-        if (i + 2 < kPvSteps) vf[(i + 2) % 3] = read_v(i + 2);
-        oacc[i & 3] = mfma_32x32x16_bf16(vf[i % 3], pf[i >> 3][(i >> 2) & 1], oacc[i & 3]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    if (do_qk) {
-      v8bf kf[3];
-      kf[0] = read_k(0);
-      kf[1] = read_k(1);
+    // Operand fragments are read kDepth MFMA steps ahead of their use (a
+    // 32x32x16 BF16 instruction lasts 32 cycles, so two steps would not cover
+    // the LDS latency), in one ring that runs from the P V steps into the
+    // Q K steps. Ring slots are compile-time constants.
+    constexpr int kDepth = 3;
+    constexpr int kRing = kDepth + 1;
+    v8bf fr[kRing];
+    // Q K steps; step i uses ring slot (B + i) % kRing
+    auto qk_steps = [&](auto base) {
+      constexpr int B = decltype(base)::value;
 #pragma unroll
       for (int i = 0; i < kQkSteps; ++i) {
-        if (i + 2 < kQkSteps) kf[(i + 2) % 3] = read_k(i + 2);
+        if (i + kDepth < kQkSteps) fr[(B + i + kDepth) % kRing] = read_k(i + kDepth);
         const int sb = i % L::kNsb;
-        s[sb] = mfma_32x32x16_bf16(kf[i % 3], qf[i / L::kNsb], i < L::kNsb ? (v16f){} : s[sb]);
+        s[sb] = mfma_32x32x16_bf16(fr[(B + i) % kRing], qf[i / L::kNsb], i < L::kNsb ? (v16f){} : s[sb]);
         __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    if (do_pv) {
+#pragma unroll
+      for (int j = 0; j < kDepth; ++j) fr[j] = read_v(j);
+#pragma unroll
+      for (int i = 0; i < kPvSteps; ++i) {
+        const int jn = i + kDepth;
+        if (jn < kPvSteps)
+          fr[jn % kRing] = read_v(jn);
+        else if (do_qk)
+          fr[jn % kRing] = read_k(jn - kPvSteps);
+        oacc[i & 3] = mfma_32x32x16_bf16(fr[i % kRing], pf[i >> 3][(i >> 2) & 1], oacc[i & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if (do_qk) {
+#pragma unroll
+      for (int j = 0; j < kDepth; ++j) fr[(kPvSteps + j) % kRing] = read_k(j);
     }
+    if (do_qk) qk_steps(std::integral_constant<int, kPvSteps>{});
     __builtin_amdgcn_s_setprio(0);
   };
 
@@ -227,19 +241,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
       lsum *= alpha;
     }
+    // P = 2^(S c - m c) rounded to BF16; the row sum adds the rounded pairs
+    // (v_dot2 against (1, 1)), i.e. exactly the weights the P V product uses
+    const v2bf ones2 = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
     for (int sb = 0; sb < L::kNsb; ++sb) {
-      float pr[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(fmaf(s[sb][r], c, nmc));
-        lsum += pr[r];
-      }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const v4i pw = {(int)pack_bf16(pr[8 * hh + 0], pr[8 * hh + 1]), (int)pack_bf16(pr[8 * hh + 2], pr[8 * hh + 3]),
-                        (int)pack_bf16(pr[8 * hh + 4], pr[8 * hh + 5]), (int)pack_bf16(pr[8 * hh + 6], pr[8 * hh + 7])};
-        pf[sb][hh] = __builtin_bit_cast(v8bf, pw);
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 8 * hh + 2 * e;
+          pw[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[sb][r], c, nmc)),
+                            __builtin_amdgcn_exp2f(fmaf(s[sb][r + 1], c, nmc)));
+          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pw[e]), ones2, lsum, false);
+        }
+        pf[sb][hh] = __builtin_bit_cast(v8bf, (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
       }
     }
   };
