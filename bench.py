@@ -118,6 +118,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known byte count for HBM counters)")
     ap.add_argument("--paths", default=",".join(PATHS))
+    ap.add_argument("--fp8-flags", type=int, default=0,
+                    help="ATTN_FLAG_* bits for the FP8 launches (1 exact P, 2 no block scaling): ablations only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
@@ -146,7 +148,8 @@ def main():
     def launch(n):
         i = inputs[n]
         dq, dk, dv = i.descale
-        fbc.flash_attn_func(i.q, i.k, i.v, i.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n])
+        ab = dict(exact_p=bool(args.fp8_flags & 1), block_scale=not (args.fp8_flags & 2)) if i.dtype == "fp8" else {}
+        fbc.flash_attn_func(i.q, i.k, i.v, i.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n], **ab)
 
     for _ in range(args.warmup):
         for n in names:
@@ -200,6 +203,11 @@ def main():
                 "frac": paths[dom]["frac_of_peak"], "traffic": measured_traffic(dom, dom_kind), "kernel": dom}
     for n in names:
         paths[n]["hbm_traffic_bytes"] = measured_traffic(n, inputs[n].dtype)
+    if args.fp8_flags:
+        # an ablation of the FP8 softmax: not the method's number, not comparable with the pages' figure
+        for n in names:
+            paths[n].pop("pages_tflops", None)
+            paths[n].pop("ratio_to_pages", None)
     cfg = {"workload": "+".join(names), "B": 1, "H": 32, "S": 32768, "Dqk": 128, "Dv": 128,
            "input": "Gaussian N(0,1), seeds 3 (fp8) and 4 (bf16), per-tensor e4m3 scales",
            "flop_count": "causal B*H*S^2*(Dqk+Dv)"}
@@ -208,6 +216,8 @@ def main():
             "vs_baseline": None, "dtype": "+".join(sorted({inputs[n].dtype for n in names})), "data": "synthetic",
             "config": cfg, "frac_of_peak": round(ideal_s / (ms_per_step * 1e-3), 4),
             "paths": paths, "roofline": roofline}
+    if args.fp8_flags:
+        line["fp8_flags"] = args.fp8_flags
     if not args.no_cpu_baseline:
         threads = min(int(os.environ.get("OMP_NUM_THREADS", "16")), os.cpu_count() or 1, 16)
         line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_rows, threads)

@@ -10,11 +10,11 @@ from __future__ import annotations
 import math
 
 from . import synth  # noqa: F401
-from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FP8_E4M3, ATTN_OK,
-                   attn_fwd, attn_fwd_ex, attn_strerror)
+from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_EXACT_P,
+                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_strerror)
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_strerror", "flash_attn_func", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
-           "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH"]
+           "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
 
 
 def _raise(code: int):
@@ -27,11 +27,12 @@ def _raise(code: int):
 
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, descale_k=None, descale_v=None,
-                    out=None):
+                    out=None, exact_p=False, block_scale=True):
     """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
     factors. Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
-    enqueued on the current stream."""
+    enqueued on the current stream. exact_p=True / block_scale=False select
+    the FP8 softmax ablations (ATTN_FLAG_EXACT_P / ATTN_FLAG_NO_BLOCKSCALE)."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -61,10 +62,11 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     ds = None
     if dtype == ATTN_FP8_E4M3 and any(x is not None for x in (descale_q, descale_k, descale_v)):
         ds = tuple(1.0 if x is None else float(x) for x in (descale_q, descale_k, descale_v))
+    flags = (ATTN_FLAG_EXACT_P if exact_p else 0) | (0 if block_scale else ATTN_FLAG_NO_BLOCKSCALE)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     with torch.cuda.device(q.device):
         rc = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, Dqk, Dv,
-                         1 if causal else 0, float(softmax_scale), dtype, ds, stream, 0)
+                         1 if causal else 0, float(softmax_scale), dtype, ds, stream, flags)
     if rc != ATTN_OK:
         _raise(rc)
     return out

@@ -12,6 +12,8 @@ ATTN_OK = 0
 ATTN_ERR_INVALID = -1
 ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_LAUNCH = -3
+ATTN_FLAG_EXACT_P = 1
+ATTN_FLAG_NO_BLOCKSCALE = 2
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8_bf16_causal.so")
 _lib = None

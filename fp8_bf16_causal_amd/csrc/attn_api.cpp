@@ -56,7 +56,7 @@ extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
     dv = descale_qkv[2];
     if (!finite_positive(dq) || !finite_positive(dk) || !finite_positive(dv)) return ATTN_ERR_INVALID;
   }
-  if (flags != 0u) return ATTN_ERR_INVALID;
+  if ((flags & ~(unsigned)(ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE)) != 0u) return ATTN_ERR_INVALID;
   const int64_t elem = dtype == ATTN_FP8_E4M3 ? 1 : 2;
   const int64_t dmax = Dqk > Dv ? Dqk : Dv;
   if ((int64_t)B * S * Hq * dmax * 2 > (INT64_C(1) << 62) || (int64_t)B * S * Hq * dmax * elem > (INT64_C(1) << 62))
@@ -72,6 +72,7 @@ extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
   if (causal != 1) return ATTN_ERR_UNSUPPORTED;
   if (dtype != ATTN_BF16 && dtype != ATTN_FP8_E4M3) return ATTN_ERR_UNSUPPORTED;
   if (!((Dqk == 128 && Dv == 128) || (Dqk == 192 && Dv == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (dtype == ATTN_BF16 && flags != 0u) return ATTN_ERR_UNSUPPORTED;
   const int dev_rc = check_device();
   if (dev_rc != ATTN_OK) return dev_rc;
 
@@ -95,7 +96,7 @@ extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the launch check below is ours
-  const hipError_t e = dtype == ATTN_FP8_E4M3 ? fbc::launch_attn_fwd_fp8(p, Dqk, (int)grid, st)
+  const hipError_t e = dtype == ATTN_FP8_E4M3 ? fbc::launch_attn_fwd_fp8(p, Dqk, (int)flags, (int)grid, st)
                                               : fbc::launch_attn_fwd_bf16(p, Dqk, (int)grid, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }
@@ -110,9 +111,9 @@ extern "C" const char* attn_strerror(int code) {
     case ATTN_OK:
       return "success";
     case ATTN_ERR_INVALID:
-      return "invalid argument (null or misaligned pointer, bad size, Hq % Hkv != 0, bad scale/descale, flags)";
+      return "invalid argument (null or misaligned pointer, bad size, Hq % Hkv != 0, bad scale/descale, unknown flags)";
     case ATTN_ERR_UNSUPPORTED:
-      return "unsupported (non-causal, unknown dtype, head dims other than 128/128 or 192/128, or not gfx950)";
+      return "unsupported (non-causal, unknown dtype, head dims other than 128/128 or 192/128, flags with BF16, or not gfx950)";
     case ATTN_ERR_LAUNCH:
       return "HIP runtime error while querying the device or launching the kernel";
     default:

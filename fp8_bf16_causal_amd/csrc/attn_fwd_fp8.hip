@@ -118,9 +118,13 @@ __device__ inline int vkey_fp8(int r) {
 // (prefetch at the end of group 0's Y_t) to slot 2t+3: each load overwrites a
 // buffer last read at least one slot before it starts, and each tile is
 // published at least one slot before it is first read.
-template <int DQK>
+// MODE: 0 for the method; bit 0 = exact e4m3 rounding of 2^x instead of the
+// Lean P code, bit 1 = no per-block exponent (ablations).
+template <int DQK, int MODE>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p) {
   using L = Fp8Layout<DQK>;
+  constexpr bool kExactP = (MODE & 1) != 0;
+  constexpr bool kBlockScale = (MODE & 2) == 0;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[L::kLds];
   uint8_t* const Kbuf = lds;                            // kStages x kKTile
   uint8_t* const Vbuf = lds + L::kStages * L::kKTile;   // kStages x kVTile
@@ -325,18 +329,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     // binades; otherwise probabilities up to 2^kLazyLog2 are encoded relative
     // to the old m, which the per-block exponent absorbs (k >= 0 keeps every
     // code <= 120). O / l does not depend on the reference point.
+    // (Without block exponents the reference max moves on every rise, so the
+    // encoded probabilities stay in [0, 1]: the plain FP8 softmax.)
+    constexpr float kLazy = kBlockScale ? kLazyLog2 : 0.0f;
     const float mt = fmaxf(ma, mb);
-    const float mn = (mt - m) * c > kLazyLog2 ? mt : m;
+    const float mn = (mt - m) * c > kLazy ? mt : m;
     const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
     m = mn;
     // block exponents: the block max lands in (2^7, 2^8]
-    const float ka = fminf(fmaxf(floorf(8.0f - (ma - mn) * c), 0.0f), 127.0f);
-    const float kb = fminf(fmaxf(floorf(8.0f - (mb - mn) * c), 0.0f), 127.0f);
-    const float bias_a = fmaf(-c8, mn, kLeanPC + 8.0f * ka);
-    const float bias_b = fmaf(-c8, mn, kLeanPC + 8.0f * kb);
-    // Lean P: code = u8(8 c s + C + 8k - 8 c m), four codes per dword, in
-    // accumulator order: P[ks] dword d holds registers 4(d%4) .. +3 of
-    // s[2 ks + d/4]
+    const float ka = kBlockScale ? fminf(fmaxf(floorf(8.0f - (ma - mn) * c), 0.0f), 127.0f) : 0.0f;
+    const float kb = kBlockScale ? fminf(fmaxf(floorf(8.0f - (mb - mn) * c), 0.0f), 127.0f) : 0.0f;
+    // Lean P: code = u8(8 c s + C + 8k - 8 c m); exact (ablation): the e4m3
+    // rounding of 2^(c s + k - c m). Four codes per dword, in accumulator
+    // order: P[ks] dword d holds registers 4(d%4) .. +3 of s[2 ks + d/4].
+    const float bias_a = kExactP ? fmaf(-c, mn, ka) : fmaf(-c8, mn, kLeanPC + 8.0f * ka);
+    const float bias_b = kExactP ? fmaf(-c, mn, kb) : fmaf(-c8, mn, kLeanPC + 8.0f * kb);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const float bias = ks == 0 ? bias_a : bias_b;
@@ -345,10 +352,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
         const v16f& sv = s[2 * ks + (d >> 2)];
         const int r0 = 4 * (d & 3);
         uint32_t w = 0;
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 0], c8, bias), 0, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 1], c8, bias), 1, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 2], c8, bias), 2, w);
-        w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 3], c8, bias), 3, w);
+        if constexpr (kExactP) {
+          const float x0 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 0], c, bias));
+          const float x1 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 1], c, bias));
+          const float x2 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 2], c, bias));
+          const float x3 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 3], c, bias));
+          w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+          w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)w, true);
+        } else {
+          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 0], c8, bias), 0, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 1], c8, bias), 1, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 2], c8, bias), 2, w);
+          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 3], c8, bias), 3, w);
+        }
         P[ks][d] = (int)w;
         if (d & 1) ld(4 * ks + (d >> 1));
       }
@@ -453,15 +469,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   }
 }
 
-template <int DQK>
+template <int DQK, int MODE>
 static hipError_t launch_fp8(const AttnParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(attn_fwd_fp8_kernel<DQK>, dim3(grid), dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((attn_fwd_fp8_kernel<DQK, MODE>), dim3(grid), dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_fp8(const AttnParams& p, int dqk, int grid, hipStream_t stream) {
-  if (dqk == 128) return launch_fp8<128>(p, grid, stream);
-  return launch_fp8<192>(p, grid, stream);
+template <int DQK>
+static hipError_t launch_fp8_mode(const AttnParams& p, int mode, int grid, hipStream_t stream) {
+  switch (mode) {
+    case 0: return launch_fp8<DQK, 0>(p, grid, stream);
+    case 1: return launch_fp8<DQK, 1>(p, grid, stream);
+    case 2: return launch_fp8<DQK, 2>(p, grid, stream);
+    default: return launch_fp8<DQK, 3>(p, grid, stream);
+  }
+}
+
+hipError_t launch_attn_fwd_fp8(const AttnParams& p, int dqk, int mode, int grid, hipStream_t stream) {
+  if (dqk == 128) return launch_fp8_mode<128>(p, mode, grid, stream);
+  return launch_fp8_mode<192>(p, mode, grid, stream);
 }
 
 }  // namespace fbc

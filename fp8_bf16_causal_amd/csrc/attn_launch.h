@@ -10,7 +10,8 @@ struct AttnParams;
 
 // One workgroup of 512 threads per (batch, query head, 256-row query block);
 // grid = B * Hq * ceil(S / 256). dqk is 128 or 192 (Dv is 128).
-hipError_t launch_attn_fwd_fp8(const AttnParams& p, int dqk, int grid, hipStream_t stream);
+// mode: ATTN_FLAG_* bits (0 = the method as the pages give it)
+hipError_t launch_attn_fwd_fp8(const AttnParams& p, int dqk, int mode, int grid, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int dqk, int grid, hipStream_t stream);
 
 }  // namespace fbc

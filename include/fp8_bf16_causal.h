@@ -54,18 +54,35 @@ extern "C" {
 /* Element type of q, k and v. out is always BF16. */
 enum { ATTN_BF16 = 0, ATTN_FP8_E4M3 = 1 };
 
+/*
+ * attn_fwd_ex flags: ablations of the FP8 softmax (dtype ATTN_FP8_E4M3 only).
+ * They reproduce the comparisons the pages draw [spbcomputers.ru ZYFA
+ * article, sections "Три приёма, которые дали ускорение" and "Точность":
+ * exact e4m3 rounding of each probability versus the one-FMA code, 5.9 versus
+ * 7.5 percent worst-case error, and matrix-core busy time; captivela.com
+ * "Zyphra Luncurkan ZYFA", section "Tiga Trik ZYFA Biar Cepat dan Akurat",
+ * third trick: per-block scaling for blocks far below the row maximum].
+ *   ATTN_FLAG_EXACT_P        each probability is 2^x evaluated in fp32 and
+ *                            rounded to e4m3 (nearest, ties to even) instead
+ *                            of the one-FMA code
+ *   ATTN_FLAG_NO_BLOCKSCALE  no per-64-key-block power of two: every block
+ *                            keeps exponent 0 (plain probabilities in [0, 1])
+ * The two may be combined.
+ */
+enum { ATTN_FLAG_EXACT_P = 1u, ATTN_FLAG_NO_BLOCKSCALE = 2u };
+
 /* Return codes. */
 enum {
   ATTN_OK = 0,
   /* a null or misaligned pointer (q, k, v, out must be 16-byte aligned), a
    * size <= 0, Hq not a multiple of Hkv, scale negative or not finite, a
-   * descale factor <= 0 or not finite, a non-zero flags word, or sizes whose
+   * descale factor <= 0 or not finite, a flags word with unknown bits, or sizes whose
    * products overflow the index types (one batch entry of q, k, v or out must
    * stay below 4 GiB; the workgroup count B*Hq*ceil(S/256) below 2^31) */
   ATTN_ERR_INVALID = -1,
   /* causal == 0 (the method is causal-only), an unknown dtype, a head-dim
-   * pair other than (Dqk, Dv) = (128, 128) or (192, 128), or a current device
-   * that is not gfx950 */
+   * pair other than (Dqk, Dv) = (128, 128) or (192, 128), flags with dtype
+   * ATTN_BF16, or a current device that is not gfx950 */
   ATTN_ERR_UNSUPPORTED = -2,
   /* the HIP runtime reported an error when querying the device or launching */
   ATTN_ERR_LAUNCH = -3
@@ -91,7 +108,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
  *   descale_qkv  host pointer to {dq, dk, dv}, or NULL for {1, 1, 1}; read
  *                during the call only
  *   stream       a hipStream_t, or NULL for the null stream
- *   flags        reserved, must be 0
+ *   flags        0, or ATTN_FLAG_* bits (FP8 only) selecting an ablation of
+ *                the FP8 softmax
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S, int Dqk,
                 int Dv, int causal, float scale, int dtype, const float* descale_qkv, void* stream,

@@ -54,7 +54,8 @@ def _call(ptrs=(P, P, P, P), descale=None, flags=0, **kw):
     dict(B=0), dict(S=0), dict(S=-3), dict(Hq=0), dict(Hkv=0), dict(Dqk=0), dict(Dv=-1), dict(Hq=6, Hkv=4),
     dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.1),
     dict(descale=(1.0, 0.0, 1.0)), dict(descale=(1.0, 1.0, float("nan"))), dict(descale=(-1.0, 1.0, 1.0)),
-    dict(flags=1), dict(B=1 << 20, S=1 << 30, Hq=1 << 10, Hkv=1 << 10), dict(S=1 << 22, Hq=1 << 12, Hkv=1 << 12),
+    dict(flags=4), dict(flags=1 << 31), dict(flags=7, dtype=fbc.ATTN_FP8_E4M3),
+    dict(B=1 << 20, S=1 << 30, Hq=1 << 10, Hkv=1 << 10), dict(S=1 << 22, Hq=1 << 12, Hkv=1 << 12),
 ])
 def test_invalid_arguments(kw):
     assert _call(**kw) == fbc.ATTN_ERR_INVALID
@@ -62,6 +63,7 @@ def test_invalid_arguments(kw):
 
 @pytest.mark.parametrize("kw", [
     dict(causal=0), dict(dtype=2), dict(dtype=-1), dict(Dqk=64, Dv=64), dict(Dqk=128, Dv=64), dict(Dqk=256, Dv=256),
+    dict(flags=fbc.ATTN_FLAG_EXACT_P), dict(flags=fbc.ATTN_FLAG_NO_BLOCKSCALE),  # the ablations are FP8-only
 ])
 def test_unsupported_arguments(kw):
     assert _call(**kw) == fbc.ATTN_ERR_UNSUPPORTED
