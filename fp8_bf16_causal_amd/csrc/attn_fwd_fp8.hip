@@ -234,7 +234,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   for (int d = 0; d < 4; ++d) oacc[d] = (v16f){};
   lacc = (v16f){};
   float m = -INFINITY;  // running max of the raw scores of query qw0 + l32
-  const float c = p.c, c8 = 8.0f * p.c;
+  // the base-2 score scale lives in a vector register: as a scalar it would be
+  // spilled and reloaded every tile under this kernel's scalar-register pressure
+  float c = p.c;
+  asm volatile("" : "+v"(c));
+  const float c8 = 8.0f * c;
 
   v16f s[4];     // S_t^T, from X_t to Y_t
   v8i P[2];      // P_t codes (64-key block ks in P[ks]), from Y_t to X_{t+1}
