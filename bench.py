@@ -76,6 +76,38 @@ def measured_traffic(workload, kind):
     return int(kv["traffic_bytes"]) if kv else None
 
 
+def time_quant_prologue(steps, warmup):
+    """The FP8 quantize prologue (attn_quantize_e4m3) on the 32K benchmark's
+    query tensor as BF16 (32768 x 32 x 128), plain and with the Hadamard
+    rotation: HBM-bound, 5 algorithmic bytes per element (two reads of the
+    BF16 input, since the per-tensor amax precedes every code, and one byte
+    written)."""
+    import torch
+
+    import fp8_bf16_causal_amd as fbc
+
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn((32768, 32, 128), generator=g, device="cuda").to(torch.bfloat16)
+    n = x.numel()
+    res = {"workload": "query tensor of fp8_mha_s32k as BF16, 32768 x 32 x 128", "bytes_per_element": 5,
+           "peak_GBps": 8000.0}
+    for had in (False, True):
+        for _ in range(warmup):
+            fbc.quantize_e4m3(x, hadamard=had)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fbc.quantize_e4m3(x, hadamard=had)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = 5.0 * n / (ms * 1e-3) / 1e9
+        key = "hadamard" if had else "plain"
+        res[key] = {"ms": round(ms, 4), "GBps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / 8000.0, 4)}
+    return res
+
+
 def causal_flops(p):
     return float(p["B"]) * p["Hq"] * p["S"] * p["S"] * (p["Dqk"] + p["Dv"])
 
@@ -118,6 +150,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known byte count for HBM counters)")
     ap.add_argument("--paths", default=",".join(PATHS))
+    ap.add_argument("--no-quant", action="store_true", help="skip the FP8 quantize-prologue timing")
+    ap.add_argument("--quant-only", action="store_true", help="time only the FP8 quantize prologue")
     ap.add_argument("--fp8-flags", type=int, default=0,
                     help="ATTN_FLAG_* bits for the FP8 launches (1 exact P, 2 no block scaling): ablations only")
     args = ap.parse_args()
@@ -132,11 +166,6 @@ def main():
 
     fbc._lib.load()
     torch.cuda.set_device(0)
-    names = args.paths.split(",")
-    inputs = {n: synth.make_config(n, device="cuda") for n in names}
-    outs = {n: torch.empty((i.shape["B"], i.shape["S"], i.shape["Hq"], i.shape["Dv"]), dtype=torch.bfloat16,
-                           device="cuda") for n, i in inputs.items()}
-
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
@@ -144,6 +173,14 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+
+    if args.quant_only:
+        print(json.dumps({"quantize_prologue": time_quant_prologue(args.steps, min(args.warmup, 20))}), flush=True)
+        return
+    names = args.paths.split(",")
+    inputs = {n: synth.make_config(n, device="cuda") for n in names}
+    outs = {n: torch.empty((i.shape["B"], i.shape["S"], i.shape["Hq"], i.shape["Dv"]), dtype=torch.bfloat16,
+                           device="cuda") for n, i in inputs.items()}
 
     def launch(n):
         i = inputs[n]
@@ -218,6 +255,8 @@ def main():
             "paths": paths, "roofline": roofline}
     if args.fp8_flags:
         line["fp8_flags"] = args.fp8_flags
+    if not args.no_quant and not args.fp8_flags:
+        line["quantize_prologue"] = time_quant_prologue(20, 5)
     if not args.no_cpu_baseline:
         threads = min(int(os.environ.get("OMP_NUM_THREADS", "16")), os.cpu_count() or 1, 16)
         line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_rows, threads)

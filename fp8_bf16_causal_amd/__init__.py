@@ -11,9 +11,10 @@ import math
 
 from . import synth  # noqa: F401
 from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_EXACT_P,
-                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_strerror)
+                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_quantize_e4m3,
+                   attn_strerror)
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_strerror", "flash_attn_func", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_quantize_e4m3", "attn_strerror", "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
            "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
 
 
@@ -70,3 +71,25 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     if rc != ATTN_OK:
         _raise(rc)
     return out
+
+
+def quantize_e4m3(x, hadamard=False):
+    """Per-tensor e4m3fn quantisation of a bfloat16 tensor [..., dim] on the
+    GPU (dim 64, 128, 192 or 256), optionally rotating each row by a Hadamard
+    transform first (for Q and K). Returns (codes as float8_e4m3fn, a device
+    float32 tensor [s, amax]); attn_fwd takes the codes with descale s.
+    Enqueued on the current stream."""
+    import torch
+
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.dim() < 1:
+        raise ValueError("x must be a contiguous bfloat16 GPU tensor")
+    dim = x.shape[-1]
+    rows = x.numel() // dim if dim else 0
+    y = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
+    scale = torch.empty(2, dtype=torch.float32, device=x.device)
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    with torch.cuda.device(x.device):
+        rc = attn_quantize_e4m3(x.data_ptr(), y.data_ptr(), scale.data_ptr(), rows, dim, 1 if hadamard else 0, stream)
+    if rc != ATTN_OK:
+        _raise(rc)
+    return y, scale

@@ -9,7 +9,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libfp8_bf16_causal.so")
-SOURCES = ["attn_api.cpp", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip"]
+SOURCES = ["attn_api.cpp", "attn_fwd_fp8.hip", "attn_fwd_bf16.hip", "attn_quant.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

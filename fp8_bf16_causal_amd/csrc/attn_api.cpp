@@ -106,7 +106,20 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
   return attn_fwd_ex(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, nullptr, nullptr, 0u);
 }
 
-extern "C" const char* attn_strerror(int code) {
+extern "C" int attn_quantize_e4m3(const void* x, void* y, float* scale, long long rows, int dim, int hadamard, void* stream) {
+  if (!x || !y || !scale) return ATTN_ERR_INVALID;
+  if (((uintptr_t)x & 1u) || ((uintptr_t)scale & 3u)) return ATTN_ERR_INVALID;
+  if (rows <= 0 || (hadamard != 0 && hadamard != 1)) return ATTN_ERR_INVALID;
+  if (dim != 64 && dim != 128 && dim != 192 && dim != 256) return ATTN_ERR_UNSUPPORTED;
+  if (rows > (long long)(INT64_MAX / 256)) return ATTN_ERR_INVALID;
+  const int dc = check_device();
+  if (dc != ATTN_OK) return dc;
+  (void)hipGetLastError();
+  const hipError_t e = fbc::launch_quantize_e4m3(x, y, scale, (int64_t)rows, dim, hadamard, (hipStream_t)stream);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+const char* attn_strerror(int code) {
   switch (code) {
     case ATTN_OK:
       return "success";

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fbc {
 
@@ -13,5 +14,10 @@ struct AttnParams;
 // mode: ATTN_FLAG_* bits (0 = the method as the pages give it)
 hipError_t launch_attn_fwd_fp8(const AttnParams& p, int dqk, int mode, int grid, hipStream_t stream);
 hipError_t launch_attn_fwd_bf16(const AttnParams& p, int dqk, int grid, hipStream_t stream);
+
+// FP8 quantize prologue: clear, amax, convert (three kernels on `stream`).
+// dim is 64, 128, 192 or 256; scale points to 2 device floats.
+hipError_t launch_quantize_e4m3(const void* x, void* y, float* scale, int64_t rows, int dim, int hadamard,
+                                hipStream_t stream);
 
 }  // namespace fbc

@@ -115,6 +115,38 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
                 int Dv, int causal, float scale, int dtype, const float* descale_qkv, void* stream,
                 unsigned flags);
 
+/*
+ * attn_quantize_e4m3: the FP8 quantize prologue. Per-tensor e4m3fn
+ * quantisation of a BF16 tensor viewed as `rows` rows of `dim` elements,
+ * optionally rotating every row by a normalised Hadamard transform first (for
+ * Q and K: one orthogonal H on both leaves Q K^T unchanged).
+ *   [spbcomputers.ru ZYFA article, section "Точность: ошибка FP8 ниже, чем у
+ *    AITER" and the FAQ entry on the Hadamard rotation; captivela.com "Zyphra
+ *    Luncurkan ZYFA", section "Akurasi Jauh Lebih Baik, Bukan Cuma Cepat":
+ *    quantising Q, K and V dominates a full model's FP8 attention error, and a
+ *    Hadamard rotation of Q and K roughly halves it.]
+ * Definition (every step in IEEE fp32): y = the row, or its Walsh-Hadamard
+ * transform in blocks of n = 128 elements (dim a multiple of 128) or n = 64,
+ * butterflies over index bits 0, 1, ... then one multiply by fp32(1/sqrt(n));
+ * amax = max |y| over the tensor; s = amax / 448 (1 if amax = 0); code =
+ * e4m3fn(y / s), rounded to nearest, ties to even. attn_fwd takes the codes
+ * with descale s.
+ *
+ *   x         device pointer to rows*dim BF16 values (2-byte aligned)
+ *   y         device pointer to rows*dim bytes, receives the e4m3fn codes
+ *   scale     device pointer to 2 floats (4-byte aligned): scale[0] receives
+ *             s, scale[1] amax; overwritten (also used as the reduction word)
+ *   rows      >= 1
+ *   dim       64, 128, 192 or 256
+ *   hadamard  0 or 1
+ *   stream    a hipStream_t, or NULL for the null stream
+ * Errors: ATTN_ERR_INVALID for a null or misaligned pointer, rows <= 0 or a
+ * hadamard flag other than 0/1; ATTN_ERR_UNSUPPORTED for another dim or a
+ * device that is not gfx950; ATTN_ERR_LAUNCH for a HIP error. Asynchronous
+ * like attn_fwd; x must not overlap y or scale.
+ */
+int attn_quantize_e4m3(const void* x, void* y, float* scale, long long rows, int dim, int hadamard, void* stream);
+
 /* A static, human-readable description of a return code (never NULL). */
 const char* attn_strerror(int code);
 
