@@ -108,7 +108,7 @@ extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, 
 
 extern "C" int attn_quantize_e4m3(const void* x, void* y, float* scale, long long rows, int dim, int hadamard, void* stream) {
   if (!x || !y || !scale) return ATTN_ERR_INVALID;
-  if (((uintptr_t)x & 1u) || ((uintptr_t)scale & 3u)) return ATTN_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(y) || ((uintptr_t)scale & 3u)) return ATTN_ERR_INVALID;
   if (rows <= 0 || (hadamard != 0 && hadamard != 1)) return ATTN_ERR_INVALID;
   if (dim != 64 && dim != 128 && dim != 192 && dim != 256) return ATTN_ERR_UNSUPPORTED;
   if (rows > (long long)(INT64_MAX / 256)) return ATTN_ERR_INVALID;

@@ -17,12 +17,15 @@
 // by the fp32 constant 1/sqrt(n); y / s and amax / 448 are correctly rounded
 // divisions.
 //
-// Layout: one wave per row, lane l holding elements 64 j + l (j < dim / 64),
-// so index bits 0-5 are lane bits (butterflies across lanes) and bit 6 is j
-// (in-lane). Three kernels on one stream: clear the amax word, reduce amax
-// (the rotated values' when rotating) with a vector atomic max on the float
-// bits, then rotate again, scale and convert. HBM-bound: 2 reads of the
-// input, 1 write of the codes.
+// Layout: the tensor is a flat array of n-element blocks (n = 128 or 64, the
+// rotation's block; whole rows hold whole blocks). A wave takes 512
+// consecutive elements per step, each lane 8 (one 16-byte load): index bits
+// 0-2 of an element are in-lane, bits 3.. are lane bits, so the butterflies
+// for bits 0-2 run in registers and the rest across 8 or 16 lanes. Three
+// kernels on one stream: clear the amax word, reduce amax (of the rotated
+// values when rotating) with one vector atomic max per workgroup on the float
+// bits, then rotate again, scale and convert (8-byte stores). HBM-bound:
+// 2 reads of the input, 1 write of the codes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -30,59 +33,64 @@
 
 namespace fbc {
 
-constexpr int kQuantThreads = 256;  // 4 waves per workgroup, one row per wave at a time
+constexpr int kQuantThreads = 256;  // 4 waves per workgroup
+constexpr int kWaveElems = 512;     // elements per wave per step, 8 per lane
 
-template <int J>
-struct RowVals {
-  float v[J];
-};
+typedef int qv4i __attribute__((ext_vector_type(4)));
+typedef int qv2i __attribute__((ext_vector_type(2)));
 
-// Load row r (lane l: elements 64 j + l), rotated if HAD (block n = 128 or 64).
-template <int J, bool HAD, int N>
-__device__ inline RowVals<J> load_row(const uint16_t* x, int64_t r, int lane) {
-  RowVals<J> a;
-  const uint16_t* row = x + r * (64 * J);
+// The 8 elements e0 .. e0+7 of lane `lane` (e0 = 8 * lane within the wave's
+// 512), rotated by the normalised Walsh-Hadamard transform of block N if HAD.
+template <bool HAD, int N>
+__device__ inline void load8(const uint16_t* x, int64_t e0, bool valid, int lane, float v[8]) {
+  qv4i w = {0, 0, 0, 0};
+  if (valid) w = *(const qv4i*)(x + e0);
 #pragma unroll
-  for (int j = 0; j < J; ++j) a.v[j] = __builtin_bit_cast(float, (uint32_t)row[64 * j + lane] << 16);
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = __builtin_bit_cast(float, (uint32_t)w[i] << 16);
+    v[2 * i + 1] = __builtin_bit_cast(float, (uint32_t)w[i] & 0xFFFF0000u);
+  }
   if constexpr (HAD) {
 #pragma unroll
-    for (int h = 1; h < 64; h <<= 1) {  // index bits 0..5: across lanes
-      const bool upper = (lane & h) != 0;
+    for (int h = 1; h < 8; h <<= 1)  // index bits 0..2: in-lane
 #pragma unroll
-      for (int j = 0; j < J; ++j) {
-        const float partner = __shfl_xor(a.v[j], h, 64);
-        a.v[j] = upper ? partner - a.v[j] : a.v[j] + partner;
-      }
-    }
-    if constexpr (N == 128) {  // index bit 6: in-lane, j even / odd
+      for (int i = 0; i < 8; ++i)
+        if ((i & h) == 0) {
+          const float p = v[i], q = v[i + h];
+          v[i] = p + q;
+          v[i + h] = p - q;
+        }
 #pragma unroll
-      for (int j = 0; j + 1 < J; j += 2) {
-        const float p = a.v[j], q = a.v[j + 1];
-        a.v[j] = p + q;
-        a.v[j + 1] = p - q;
+    for (int hl = 1; hl < N / 8; hl <<= 1) {  // index bits 3..: across lanes
+      const bool upper = (lane & hl) != 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float partner = __shfl_xor(v[i], hl, 64);
+        v[i] = upper ? partner - v[i] : v[i] + partner;
       }
     }
     const float norm = N == 128 ? 0.08838834764831845f : 0.125f;  // fp32(1/sqrt(N))
 #pragma unroll
-    for (int j = 0; j < J; ++j) a.v[j] *= norm;
+    for (int i = 0; i < 8; ++i) v[i] *= norm;
   }
-  return a;
 }
 
 __global__ void quant_clear_kernel(float* scale) {
   if (threadIdx.x == 0) scale[1] = 0.0f;
 }
 
-template <int J, bool HAD, int N>
-__global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint16_t* x, float* scale, int64_t rows) {
+template <bool HAD, int N>
+__global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint16_t* x, float* scale, int64_t n) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kQuantThreads / 64);
   float m = 0.0f;
-  for (int64_t r = wave; r < rows; r += nwaves) {
-    const RowVals<J> a = load_row<J, HAD, N>(x, r, lane);
+  for (int64_t base = wave * kWaveElems; base < n; base += nwaves * kWaveElems) {
+    const int64_t e0 = base + 8 * lane;
+    float v[8];
+    load8<HAD, N>(x, e0, e0 < n, lane, v);
 #pragma unroll
-    for (int j = 0; j < J; ++j) m = fmaxf(m, fabsf(a.v[j]));
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
   }
 #pragma unroll
   for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
@@ -100,57 +108,51 @@ __global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint16_
   }
 }
 
-template <int J, bool HAD, int N>
+template <bool HAD, int N>
 __global__ __launch_bounds__(kQuantThreads) void quant_convert_kernel(const uint16_t* x, uint8_t* y, float* scale,
-                                                                      int64_t rows) {
+                                                                      int64_t n) {
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kQuantThreads / 64);
   const float amax = scale[1];
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
-  for (int64_t r = wave; r < rows; r += nwaves) {
-    const RowVals<J> a = load_row<J, HAD, N>(x, r, lane);
-    uint8_t* row = y + r * (64 * J);
+  for (int64_t base = wave * kWaveElems; base < n; base += nwaves * kWaveElems) {
+    const int64_t e0 = base + 8 * lane;
+    const bool valid = e0 < n;
+    float v[8];
+    load8<HAD, N>(x, e0, valid, lane, v);
+    qv2i out;
 #pragma unroll
-    for (int j = 0; j < J; ++j) {
-      const float q = a.v[j] / s;
-      row[64 * j + lane] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(q, 0.0f, 0, false) & 0xFF);
+    for (int i = 0; i < 2; ++i) {
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i] / s, v[4 * i + 1] / s, 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i + 2] / s, v[4 * i + 3] / s, w, true);
+      out[i] = w;
     }
+    if (valid) *(qv2i*)(y + e0) = out;
   }
 }
 
-template <int J, bool HAD, int N>
-static hipError_t launch_quant_t(const void* x, void* y, float* scale, int64_t rows, hipStream_t stream) {
-  const int64_t waves_needed = rows;
-  int64_t blocks = (waves_needed + kQuantThreads / 64 - 1) / (kQuantThreads / 64);
+template <bool HAD, int N>
+static hipError_t launch_quant_t(const void* x, void* y, float* scale, int64_t n, hipStream_t stream) {
+  int64_t blocks = (n + kWaveElems * (kQuantThreads / 64) - 1) / (kWaveElems * (kQuantThreads / 64));
   if (blocks > 16384) blocks = 16384;
   // the reduction grid is smaller: its atomics serialise at one address
   const int64_t rblocks = blocks < 1024 ? blocks : 1024;
   hipLaunchKernelGGL(quant_clear_kernel, dim3(1), dim3(64), 0, stream, scale);
-  hipLaunchKernelGGL((quant_amax_kernel<J, HAD, N>), dim3((unsigned)rblocks), dim3(kQuantThreads), 0, stream,
-                     (const uint16_t*)x, scale, rows);
-  hipLaunchKernelGGL((quant_convert_kernel<J, HAD, N>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
-                     (const uint16_t*)x, (uint8_t*)y, scale, rows);
+  hipLaunchKernelGGL((quant_amax_kernel<HAD, N>), dim3((unsigned)rblocks), dim3(kQuantThreads), 0, stream,
+                     (const uint16_t*)x, scale, n);
+  hipLaunchKernelGGL((quant_convert_kernel<HAD, N>), dim3((unsigned)blocks), dim3(kQuantThreads), 0, stream,
+                     (const uint16_t*)x, (uint8_t*)y, scale, n);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_e4m3(const void* x, void* y, float* scale, int64_t rows, int dim, int hadamard,
                                 hipStream_t stream) {
-  switch (dim) {
-    case 64:
-      return hadamard ? launch_quant_t<1, true, 64>(x, y, scale, rows, stream)
-                      : launch_quant_t<1, false, 64>(x, y, scale, rows, stream);
-    case 128:
-      return hadamard ? launch_quant_t<2, true, 128>(x, y, scale, rows, stream)
-                      : launch_quant_t<2, false, 128>(x, y, scale, rows, stream);
-    case 192:
-      return hadamard ? launch_quant_t<3, true, 64>(x, y, scale, rows, stream)
-                      : launch_quant_t<3, false, 64>(x, y, scale, rows, stream);
-    default:
-      return hadamard ? launch_quant_t<4, true, 128>(x, y, scale, rows, stream)
-                      : launch_quant_t<4, false, 128>(x, y, scale, rows, stream);
-  }
+  const int64_t n = rows * dim;  // a multiple of 64: blocks of 64 (and of 128 when dim is) never straddle rows
+  if (dim % 128 == 0)
+    return hadamard ? launch_quant_t<true, 128>(x, y, scale, n, stream) : launch_quant_t<false, 128>(x, y, scale, n, stream);
+  return hadamard ? launch_quant_t<true, 64>(x, y, scale, n, stream) : launch_quant_t<false, 64>(x, y, scale, n, stream);
 }
 
 }  // namespace fbc

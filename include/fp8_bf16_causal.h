@@ -132,8 +132,9 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
  * e4m3fn(y / s), rounded to nearest, ties to even. attn_fwd takes the codes
  * with descale s.
  *
- *   x         device pointer to rows*dim BF16 values (2-byte aligned)
- *   y         device pointer to rows*dim bytes, receives the e4m3fn codes
+ *   x         device pointer to rows*dim BF16 values (16-byte aligned)
+ *   y         device pointer to rows*dim bytes (16-byte aligned), receives the
+ *             e4m3fn codes
  *   scale     device pointer to 2 floats (4-byte aligned): scale[0] receives
  *             s, scale[1] amax; overwritten (also used as the reduction word)
  *   rows      >= 1

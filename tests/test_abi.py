@@ -86,7 +86,7 @@ def test_binding_has_no_cpu_path():
 @pytest.mark.parametrize("args,code", [
     ((0, P, P, 10, 128, 0), fbc.ATTN_ERR_INVALID), ((P, 0, P, 10, 128, 0), fbc.ATTN_ERR_INVALID),
     ((P, P, 0, 10, 128, 0), fbc.ATTN_ERR_INVALID), ((P + 1, P, P, 10, 128, 0), fbc.ATTN_ERR_INVALID),
-    ((P, P, P + 2, 10, 128, 0), fbc.ATTN_ERR_INVALID), ((P, P, P, 0, 128, 0), fbc.ATTN_ERR_INVALID),
+    ((P, P, P + 2, 10, 128, 0), fbc.ATTN_ERR_INVALID), ((P, P + 8, P, 10, 128, 0), fbc.ATTN_ERR_INVALID), ((P, P, P, 0, 128, 0), fbc.ATTN_ERR_INVALID),
     ((P, P, P, -4, 128, 1), fbc.ATTN_ERR_INVALID), ((P, P, P, 10, 128, 2), fbc.ATTN_ERR_INVALID),
     ((P, P, P, 10, 96, 0), fbc.ATTN_ERR_UNSUPPORTED), ((P, P, P, 10, 512, 1), fbc.ATTN_ERR_UNSUPPORTED),
 ])
