@@ -132,6 +132,13 @@ __device__ inline void gl_load_lds16(const uint8_t* src, uint8_t* lds_base) {
 // s_waitcnt vmcnt(0): every vector-memory load of this wave (including
 // direct-to-LDS ones) has completed.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): all but this wave's N most recently issued vector-memory
+// loads have completed (they complete in issue order).
+template <int N>
+__device__ inline void wait_vmem_all_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt(((N >> 4) << 14) | 0x0F70 | (N & 15));
+}
 // Workgroup barrier without a memory fence. __syncthreads() also waits for
 // every outstanding global load of the wave (vmcnt(0)), which would stall each
 // slot on the direct-to-LDS loads still in flight for a later slot. This one
@@ -214,9 +221,13 @@ struct TileLoader {
     if constexpr (kRem != 0) {
       const int rw = (wave + ROT) % NW;
       rem_inst = rw < kRem ? kFull * NW + rw : -1;
-      off[kFull] = lane_offset(rem_inst < 0 ? 0 : rem_inst, lane, row_stride, key_of);
+      // a wave without a remainder instruction issues one anyway, out of
+      // range (its lanes write zeros to a spare LDS area): see issue_spare
+      off[kFull] = rem_inst < 0 ? kOutOfRange : lane_offset(rem_inst, lane, row_stride, key_of);
     }
   }
+  // a source offset past any buffer resource's range (ranges stay below 2^31)
+  static constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
   // r: resource whose byte 0 is the tile's first key row and whose range ends
   // with the sequence's last row
   __device__ void issue(rsrc_t r, uint8_t* lds_tile) const {
@@ -229,6 +240,16 @@ struct TileLoader {
       buf_load_lds16(r, off[u], lds_tile + (wave + NW * u) * 1024);
     else if (rem_inst >= 0)
       buf_load_lds16(r, off[kFull], lds_tile + rem_inst * 1024);
+  }
+  // The same without a branch: every wave issues kRegs instructions (so a
+  // vmcnt wait can count one tile's loads); one without a remainder
+  // instruction sends its last to `spare` (1 KiB of LDS nobody reads), from
+  // out of range, so it writes zeros there.
+  __device__ void issue_spare(rsrc_t r, uint8_t* lds_tile, uint8_t* spare, int u) const {
+    if (u < kFull)
+      buf_load_lds16(r, off[u], lds_tile + (wave + NW * u) * 1024);
+    else
+      buf_load_lds16(r, off[kFull], rem_inst >= 0 ? lds_tile + rem_inst * 1024 : spare);
   }
 };
 

@@ -70,7 +70,8 @@ struct Fp8Layout {
   static constexpr int kKTile = kKLoTile + kKHiTile;
   static constexpr int kVTile = kBK * kVStride;
   static constexpr int kStages = 3;                   // buffers per operand
-  static constexpr int kLoop = kStages * (kKTile + kVTile);
+  static constexpr int kSpare = kStages * (kKTile + kVTile);  // 1 KiB target of idle loads
+  static constexpr int kLoop = kSpare + 1024;
   static constexpr int kEpi = kWaves * kQW * kOStride;
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
 };
@@ -108,16 +109,19 @@ __device__ inline int vkey_fp8(int r) {
 // fragments are read at the end of Y_{t-1}, so the matrix cores start at the
 // barrier.
 //
-// K/V staging (three buffers per operand): each group copies one operand,
-// from its softmax phases, one direct-to-LDS instruction at a time spread
-// through the code generation (a burst at the start of the phase would hold
-// up its vector instructions behind the memory instructions). Group 1 loads
-// V_{t+1} during Y_{t-1} (slot 2t) and waits for it at the end of X_t (slot
-// 2t+1); group 0 loads K_{t+2} during Y_t (slot 2t+1) and waits at the end of
-// X_{t+1} (slot 2t+2). K_t is read in slots 2t and 2t+1, V_t from slot 2t+1
-// (prefetch at the end of group 0's Y_t) to slot 2t+3: each load overwrites a
-// buffer last read at least one slot before it starts, and each tile is
-// published at least one slot before it is first read.
+// K/V staging (three buffers per operand): each group copies one operand with
+// direct-to-LDS instructions issued together at the start of its softmax
+// phase (issued later, spread through the phase or in the matrix phase, they
+// measured slower). Group 1 loads V_{t+1} during Y_{t-1} (slot 2t); group 0
+// loads K_{t+2} during Y_t (slot 2t+1). K_t is read in slots 2t and 2t+1, V_t
+// from slot 2t+1 (prefetch at the end of group 0's Y_t) to slot 2t+3: each
+// load overwrites a buffer last read at least one slot before it starts. A
+// wave waits for a tile at the end of the softmax phase of the slot before
+// the tile's first read, with the tile it has just issued still in flight
+// (vmcnt = one tile's loads): about two slots from issue to wait. Every
+// softmax phase issues the same loads, also for tiles past the workgroup's
+// last (empty range: zeros into a free buffer), so that no branch surrounds
+// them.
 // MODE: 0 for the method; bit 0 = exact e4m3 rounding of 2^x instead of the
 // Lean P code, bit 1 = no per-block exponent (ablations).
 template <int DQK, int MODE>
@@ -175,20 +179,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   constexpr int kKLoads = decltype(kld)::kRegs + (L::kHi ? decltype(khld)::kRegs : 0);
   constexpr int kVLoads = decltype(vld)::kRegs;
   // load u of this wave's share of K tile t (u = 0 .. kKLoads-1)
+  // Tiles t >= n_tiles (past the workgroup's last tile) are loaded too, with
+  // an empty range: zeros into a buffer the schedule has already freed, so
+  // the loads need no branch.
+  uint8_t* const spare = lds + L::kSpare;
   auto load_k = [&](int t, int u) {
     uint8_t* Kl = Kbuf + ring_offset<L::kStages>(t, L::kKTile);
     const int k0 = t * L::kBK;
     const uint8_t* src = Kg + (size_t)k0 * k_rs;
-    const uint32_t bytes = (uint32_t)(S - k0) * k_rs;  // through the end of key row S - 1's slot
+    const bool live = t < n_tiles;
+    const uint32_t bytes = live ? (uint32_t)(S - k0) * k_rs : 0u;  // through the end of key row S - 1's slot
     if (u < decltype(kld)::kRegs)
-      kld.issue_one(make_rsrc(src, bytes), Kl, u);
+      kld.issue_spare(make_rsrc(src, bytes), Kl, spare, u);
     else if constexpr (L::kHi)
-      khld.issue_one(make_rsrc(src + 128, bytes - 128), Kl + L::kKLoTile, u - decltype(kld)::kRegs);
+      khld.issue_spare(make_rsrc(src + 128, live ? bytes - 128 : 0u), Kl + L::kKLoTile, spare,
+                       u - decltype(kld)::kRegs);
   };
   auto load_v = [&](int t, int u) {
     uint8_t* Vl = Vbuf + ring_offset<L::kStages>(t, L::kVTile);
     const int k0 = t * L::kBK;
-    vld.issue_one(make_rsrc(Vg + (size_t)k0 * v_rs, (uint32_t)(S - k0) * v_rs), Vl, u);
+    const uint32_t bytes = t < n_tiles ? (uint32_t)(S - k0) * v_rs : 0u;
+    vld.issue_spare(make_rsrc(Vg + (size_t)k0 * v_rs, bytes), Vl, spare, u);
   };
 
   // V^T operand of O^T = V^T P^T (32x32x64): A lane (dv row i, half g) byte
@@ -299,11 +310,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     __builtin_amdgcn_s_setprio(0);
   };
   // Y_t: the softmax phase of tile t. ld(u), u = 0..7, issues this wave's
-  // u-th tile load of the slot (or nothing); the calls are spread through the
-  // code generation.
+  // u-th tile load of the slot (or nothing).
   auto phase_y = [&](int tt, auto&& ld) {
     // ================= Y_tt: softmax phase
     const int k0 = tt * L::kBK;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) ld(u);  // this slot's tile loads, first
+    __builtin_amdgcn_sched_barrier(0);
     if (k0 + L::kBK - 1 > qw0) {  // the tile crosses this wave's diagonal
       const int qi = qw0 + l32;
 #pragma unroll
@@ -340,6 +353,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     const float mn = (mt - m) * c > kLazy ? mt : m;
     const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
     m = mn;
+    // rescale the accumulators when the running max rose
+    if (__any(alpha != 1.0f)) {
+      // keep this a real branch: the multiplies are skipped on most tiles
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
+      lacc *= alpha;
+    }
     // block exponents: the block max lands in (2^7, 2^8]
     const float ka = kBlockScale ? fminf(fmaxf(floorf(8.0f - (ma - mn) * c), 0.0f), 127.0f) : 0.0f;
     const float kb = kBlockScale ? fminf(fmaxf(floorf(8.0f - (mb - mn) * c), 0.0f), 127.0f) : 0.0f;
@@ -370,19 +391,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
           w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 3], c8, bias), 3, w);
         }
         P[ks][d] = (int)w;
-        if (d & 1) ld(4 * ks + (d >> 1));
+
       }
     }
     sc[0] = 127 - (int)ka;
     sc[1] = 127 - (int)kb;
-    // rescale the accumulators when the running max rose
-    if (__any(alpha != 1.0f)) {
-      // keep this a real branch: the multiplies are skipped on most tiles
-      asm volatile("" ::: "memory");
-#pragma unroll
-      for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
-      lacc *= alpha;
-    }
     // the first two V fragments of X_{tt+1} (V_tt is resident: see above),
     // read after the codes so that S and the fragments are never live together
     __builtin_amdgcn_sched_barrier(0);
@@ -398,14 +411,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
 #pragma unroll
     for (int u = 0; u < kKLoads; ++u) {
       load_k(0, u);
-      if (n_tiles > 1) load_k(1, u);
+      load_k(1, u);
     }
   } else {
     vld.init(v_rs, gw, lane, vkey_fp8);
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
       load_v(0, u);
-      if (n_tiles > 1) load_v(1, u);
+      load_v(1, u);
     }
   }
   wait_vmem();
@@ -421,30 +434,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
       phase_x(t);                              // slot 2t: X_t
-      wait_vmem();                             // K_{t+1}, loaded in slot 2t-1
       lds_barrier();
       if (t < n_tiles) {                       // slot 2t + 1: Y_t, loads K_{t+2}
-        const bool ldk = t + 2 < n_tiles;
         phase_y(t, [&](int u) {
-          if (u < kKLoads && ldk) load_k(t + 2, u);
+          if (u < kKLoads) load_k(t + 2, u);
         });
+        wait_vmem_all_but<kKLoads>();          // K_{t+1} (loaded in slot 2t-1), first read in slot 2t+2
       }
       lds_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
       if (t >= 1) {                            // slot 2t: Y_{t-1}, loads V_{t+1}
-        const bool ldv = t + 1 < n_tiles;
         phase_y(t - 1, [&](int u) {
-          if (u < kVLoads && ldv) load_v(t + 1, u);
+          if (u < kVLoads) load_v(t + 1, u);
         });
+        wait_vmem_all_but<kVLoads>();          // V_t (loaded in slot 2t-2), first read in slot 2t+1
       }
       lds_barrier();
       phase_x(t);                              // slot 2t + 1: X_t
-      wait_vmem();                             // V_{t+1}, loaded in slot 2t
       lds_barrier();
     }
   }
+  // the last loads (of tiles past the range) write LDS that the epilogue reuses
+  wait_vmem();
+  lds_barrier();
 
   // ---- epilogue: O / l * dv -> BF16, staged through LDS for coalesced rows.
   uint8_t* Ol = lds + wave * kQW * kOStride;
