@@ -113,6 +113,26 @@ __device__ inline float sum_xor32(float x) {
   return as_f(r[0]) + as_f(r[1]);
 }
 
+// Causal mask of one 32x32 block of S^T (32 keys x 32 queries, accumulator
+// layout): register r of lane (query l32, half g) holds key 8 (r/4) + 4 g +
+// r%4 of the block. With d = (query - first key of the block) - 4 g, that key
+// is hidden iff d < 8 (r/4) + r%4, and its score becomes -inf. One element at
+// a time through VCC, two wait states between the compare and the select: the
+// compiler's own form keeps 16 lane masks in scalar register pairs at once,
+// which crowds the scalar register file of these kernels.
+__device__ inline void mask_block_causal(v16f& s, int d) {
+  const float ninf = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    float x = s[r];
+    asm volatile("v_cmp_gt_i32 vcc, %2, %1\n\ts_nop 1\n\tv_cndmask_b32 %0, %0, %3, vcc"
+                 : "+v"(x)
+                 : "v"(d), "i"(8 * (r >> 2) + (r & 3)), "v"(ninf)
+                 : "vcc");
+    s[r] = x;
+  }
+}
+
 
 __device__ inline v2i lds_read_tr8(const uint8_t* p) {
   return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(lds_u8*)p);

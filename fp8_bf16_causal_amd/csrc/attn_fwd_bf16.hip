@@ -211,14 +211,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   auto phase_y = [&](int tt) {
     const int k0 = tt * BK;
     if (k0 + BK - 1 > qw0) {  // the tile crosses this wave's diagonal
-      const int qi = qw0 + l32;
+      const int d = qw0 - k0 + l32 - 4 * g;
 #pragma unroll
-      for (int sb = 0; sb < L::kNsb; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key > qi) s[sb][r] = -INFINITY;
-        }
+      for (int sb = 0; sb < L::kNsb; ++sb) mask_block_causal(s[sb], d - 32 * sb);
     }
     float mt = s[0][0];
 #pragma unroll

@@ -318,25 +318,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     for (int u = 0; u < 8; ++u) ld(u);  // this slot's tile loads, first
     __builtin_amdgcn_sched_barrier(0);
     if (k0 + L::kBK - 1 > qw0) {  // the tile crosses this wave's diagonal (or lies past it)
-      // key k0 + 32 sb + 8 (r/4) + 4 g + r%4 is hidden from query qw0 + l32
-      // iff d < 32 sb + 8 (r/4) + r%4, d = qw0 - k0 + l32 - 4 g. One element
-      // at a time through VCC (two wait states between the compare and the
-      // select): 64 lane masks at once would crowd the scalar registers, and
-      // the compiler's own forms of this step upset the vector-register
-      // allocation of the whole loop.
       const int d = qw0 - k0 + l32 - 4 * g;
-      const float ninf = -INFINITY;
 #pragma unroll
-      for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = s[sb][r];
-          asm volatile("v_cmp_gt_i32 vcc, %2, %1\n\ts_nop 1\n\tv_cndmask_b32 %0, %0, %3, vcc"
-                       : "+v"(x)
-                       : "v"(d), "i"(32 * sb + 8 * (r >> 2) + (r & 3)), "v"(ninf)
-                       : "vcc");
-          s[sb][r] = x;
-        }
+      for (int sb = 0; sb < 4; ++sb) mask_block_causal(s[sb], d - 32 * sb);
     }
     // per-(row, 64-key block) maxima and the running max
     float ma = s[0][0], mb = s[2][0];
