@@ -46,6 +46,9 @@ def _load():
     lib.oracle_attn_f64.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64, f64, f64, f64, vp, i64,
                                     vp, i32]
     lib.oracle_attn_f64.restype = i32
+    lib.oracle_attn_lse_f64.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64, f64, f64, f64, vp, i64,
+                                        vp, vp, i32]
+    lib.oracle_attn_lse_f64.restype = i32
     lib.oracle_attn_probs_f64.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, f64, f64, f64, i32, i32, vp]
     lib.oracle_attn_probs_f64.restype = i32
     _lib = lib
@@ -77,12 +80,13 @@ def num_threads(requested: int = 0) -> int:
 
 
 def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, scale: float, dq: float = 1.0,
-              dk: float = 1.0, dv: float = 1.0, rows=None, nthreads: int = 0) -> np.ndarray:
+              dk: float = 1.0, dv: float = 1.0, rows=None, nthreads: int = 0, return_lse: bool = False):
     """Exact causal attention, fp64.
 
     q [B,S,Hq,Dqk], k [B,S,Hkv,Dqk], v [B,S,Hkv,Dv]: raw codes (uint16 bf16 or
     uint8 e4m3fn). rows: None (returns [B,S,Hq,Dv]) or an int array [n,3] of
-    (b, h, i) (returns [n,Dv]).
+    (b, h, i) (returns [n,Dv]). With return_lse, also the natural log-sum-exp
+    of each row's logits scale*dq*dk*<q_i, k_j> over j <= i ([B,Hq,S], or [n]).
     """
     lib = _load()
     q, k, v = _codes(q, dtype), _codes(k, dtype), _codes(v, dtype)
@@ -92,17 +96,19 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, scale: fl
         raise ValueError("shape mismatch")
     if rows is None:
         out = np.empty((B, S, Hq, Dv), dtype=np.float64)
+        lse = np.empty((B, Hq, S), dtype=np.float64) if return_lse else None
         rp, n = None, 0
     else:
         rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
         out = np.empty((rows.shape[0], Dv), dtype=np.float64)
+        lse = np.empty((rows.shape[0],), dtype=np.float64) if return_lse else None
         rp, n = rows.ctypes.data, rows.shape[0]
-    rc = lib.oracle_attn_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, B, Hq, Hkv, S, Dqk, Dv,
-                             float(scale), float(dq), float(dk), float(dv), rp, n, out.ctypes.data,
-                             int(nthreads))
+    rc = lib.oracle_attn_lse_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, B, Hq, Hkv, S, Dqk, Dv,
+                                 float(scale), float(dq), float(dk), float(dv), rp, n, out.ctypes.data,
+                                 lse.ctypes.data if return_lse else None, int(nthreads))
     if rc != 0:
-        raise ValueError("oracle_attn_f64 rejected its arguments")
-    return out
+        raise ValueError("oracle_attn_lse_f64 rejected its arguments")
+    return (out, lse) if return_lse else out
 
 
 def probs(q: np.ndarray, k: np.ndarray, dtype: int, scale: float, b: int = 0, h: int = 0, dq: float = 1.0,

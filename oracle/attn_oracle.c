@@ -85,14 +85,16 @@ typedef struct {
   const int32_t* row_h;
   const int32_t* row_i;
   double* const* row_out;
+  double* const* row_lse; /* NULL, or where each row's log-sum-exp goes */
   int64_t nrows;
   /* work distribution */
   int64_t next;
   pthread_mutex_t lock;
 } job_t;
 
-/* One output row: the definition of causal softmax attention, in fp64. */
-static void one_row(const job_t* J, int h, int i, double* out, double* qrow, double* w) {
+/* One output row: the definition of causal softmax attention, in fp64; also
+ * the row's log-sum-exp ln sum_j exp(s_j) = m + ln l when lse is not NULL. */
+static void one_row(const job_t* J, int h, int i, double* out, double* lse, double* qrow, double* w) {
   const int Dqk = J->Dqk, Dv = J->Dv;
   size_t qoff = (((size_t)J->b * J->S + i) * J->Hq + h) * Dqk;
   for (int d = 0; d < Dqk; ++d) qrow[d] = decode_elem(J->q, J->dtype, qoff + d);
@@ -118,6 +120,7 @@ static void one_row(const job_t* J, int h, int i, double* out, double* qrow, dou
     for (int d = 0; d < Dv; ++d) out[d] += wj * vr[d];
   }
   for (int d = 0; d < Dv; ++d) out[d] = J->dv * out[d] / l;
+  if (lse) *lse = m + log(l);
 }
 
 static void* worker(void* arg) {
@@ -135,7 +138,7 @@ static void* worker(void* arg) {
     r = J->next++;
     pthread_mutex_unlock(&J->lock);
     if (r >= J->nrows) break;
-    one_row(J, J->row_h[r], J->row_i[r], J->row_out[r], qrow, w);
+    one_row(J, J->row_h[r], J->row_i[r], J->row_out[r], J->row_lse ? J->row_lse[r] : NULL, qrow, w);
   }
   free(qrow);
   free(w);
@@ -149,19 +152,22 @@ int oracle_num_threads(int requested) {
 }
 
 /*
- * oracle_attn_f64: exact causal attention on the given inputs.
+ * oracle_attn_lse_f64: exact causal attention on the given inputs, and the
+ * natural log-sum-exp of each row's scores (the logits scale*dq*dk*<q_i, k_j>,
+ * j <= i). oracle_attn_f64 is the same without the log-sum-exp.
  *
  *   q [B][S][Hq][Dqk], k [B][S][Hkv][Dqk], v [B][S][Hkv][Dv]: raw element codes
  *   (uint16 bfloat16 when dtype == 0, uint8 e4m3fn when dtype == 1), host memory.
  *   scale: softmax scale; dq, dk, dv: per-tensor dequantisation factors (1 for BF16).
- *   rows: NULL for every row, giving out [B][S][Hq][Dv]; otherwise nrows triples
- *   (b, h, i) with out [nrows][Dv].
+ *   rows: NULL for every row, giving out [B][S][Hq][Dv] and lse [B][Hq][S];
+ *   otherwise nrows triples (b, h, i) with out [nrows][Dv] and lse [nrows].
+ *   lse: NULL, or where the log-sum-exps go.
  *   nthreads: worker threads, 0 for every online core.
  * Returns 0, or -1 on invalid arguments / allocation failure.
  */
-int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int S,
-                    int Dqk, int Dv, double scale, double dq, double dk, double dv, const int64_t* rows,
-                    int64_t nrows, double* out, int nthreads) {
+int oracle_attn_lse_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int S,
+                        int Dqk, int Dv, double scale, double dq, double dk, double dv, const int64_t* rows,
+                        int64_t nrows, double* out, double* lse, int nthreads) {
   if (!q || !k || !v || !out) return -1;
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP8_E4M3) return -1;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Dqk <= 0 || Dv <= 0 || Hq % Hkv) return -1;
@@ -180,9 +186,10 @@ int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int 
   int32_t* rh = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total ? total : 1));
   int32_t* ri = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total ? total : 1));
   double** ro = (double**)malloc(sizeof(double*) * (size_t)(total ? total : 1));
+  double** rl = (double**)malloc(sizeof(double*) * (size_t)(total ? total : 1));
   pthread_t* th = (pthread_t*)malloc(sizeof(pthread_t) * (size_t)nthreads);
   int rc = 0;
-  if (!kd || !vd || !rh || !ri || !ro || !th) {
+  if (!kd || !vd || !rh || !ri || !ro || !rl || !th) {
     rc = -1;
     goto done;
   }
@@ -197,6 +204,7 @@ int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int 
           rh[n] = (int32_t)rows[3 * r + 1];
           ri[n] = (int32_t)rows[3 * r + 2];
           ro[n] = out + (size_t)r * Dv;
+          rl[n] = lse ? lse + r : NULL;
           ++n;
         }
       } else {
@@ -205,6 +213,7 @@ int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int 
             rh[n] = h;
             ri[n] = i;
             ro[n] = out + (((size_t)b * S + i) * Hq + h) * Dv;
+            rl[n] = lse ? lse + ((size_t)b * Hq + h) * S + i : NULL;
             ++n;
           }
       }
@@ -219,7 +228,7 @@ int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int 
       J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.S = S;
       J.Dqk = Dqk; J.Dv = Dv; J.score_scale = scale * dq * dk; J.dv = dv;
       J.kd = kd; J.vd = vd; J.b = b; J.g = g;
-      J.row_h = rh; J.row_i = ri; J.row_out = ro; J.nrows = n; J.next = 0;
+      J.row_h = rh; J.row_i = ri; J.row_out = ro; J.row_lse = lse ? rl : NULL; J.nrows = n; J.next = 0;
       pthread_mutex_init(&J.lock, NULL);
       int nt = (int64_t)nthreads > n ? (int)n : nthreads, started = 0;
       for (int t = 0; t < nt; ++t)
@@ -234,8 +243,15 @@ int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int 
     }
   }
 done:
-  free(kd); free(vd); free(rh); free(ri); free(ro); free(th);
+  free(kd); free(vd); free(rh); free(ri); free(ro); free(rl); free(th);
   return rc;
+}
+
+int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int S,
+                    int Dqk, int Dv, double scale, double dq, double dk, double dv, const int64_t* rows,
+                    int64_t nrows, double* out, int nthreads) {
+  return oracle_attn_lse_f64(q, k, v, dtype, B, Hq, Hkv, S, Dqk, Dv, scale, dq, dk, dv, rows, nrows, out, NULL,
+                             nthreads);
 }
 
 /*

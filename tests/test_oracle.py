@@ -218,3 +218,79 @@ def test_oracle_rejects_bad_arguments():
         oracle.attention(q, k[:, :, :2], v[:, :, :2], oracle.BF16, 1.0)  # Hq % Hkv != 0
     with pytest.raises(TypeError):
         oracle.attention(q.astype(np.uint8), k, v, oracle.BF16, 1.0)
+
+
+# ---------------------------------------------------------------- log-sum-exp (per-row LSE output)
+
+def _oracle_lse(inp, rows=None, nthreads=2):
+    dt = oracle.BF16 if inp.dtype == "bf16" else oracle.FP8_E4M3
+    dq, dk, dv = inp.descale
+    return oracle.attention(synth.raw_codes(inp.q), synth.raw_codes(inp.k), synth.raw_codes(inp.v), dt,
+                            inp.scale, dq, dk, dv, rows=rows, nthreads=nthreads, return_lse=True)
+
+
+def _brute_force_lse(qd, kd, scale):
+    """ln sum_{j<=i} exp(scale <q_i, k_j>) per (b, h, i), materialised with
+    math.fsum and written independently of the oracle."""
+    B, S, Hq, D = qd.shape
+    rep = Hq // kd.shape[2]
+    lse = np.zeros((B, Hq, S))
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(S):
+                z = [scale * math.fsum(qd[b, i, h, d] * kd[b, j, h // rep, d] for d in range(D)) for j in range(i + 1)]
+                top = max(z)
+                lse[b, h, i] = top + math.log(math.fsum(math.exp(x - top) for x in z))
+    return lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("S,Hq,Hkv,D", [(1, 1, 1, 4), (9, 2, 1, 8), (16, 4, 2, 8)])
+def test_lse_matches_brute_force(dtype, S, Hq, Hkv, D):
+    inp = synth.make_inputs(B=2, S=S, Hq=Hq, Hkv=Hkv, Dqk=D, Dv=D, dtype=dtype, seed=S * 11 + Hq)
+    qd, kd, _ = (t.numpy() for t in _decoded(inp))
+    out, lse = _oracle_lse(inp)
+    assert lse.shape == (2, Hq, S)
+    assert np.max(np.abs(lse - _brute_force_lse(qd, kd, inp.scale))) <= 1e-12
+    assert np.array_equal(out, _oracle(inp))  # the output does not change with the extra result
+
+
+def test_lse_closed_forms():
+    """Equal scores (Q = 0): every visible key has weight 1, so lse_i = ln(i+1).
+    Row 0 sees only key 0: lse_0 = scale <q_0, k_0>."""
+    inp = synth.make_inputs(B=1, S=40, Hq=2, Hkv=1, Dqk=64, Dv=64, dtype="bf16", seed=12)
+    q0 = inp.q.clone()
+    inp.q.zero_()
+    _, lse = _oracle_lse(inp)
+    assert np.max(np.abs(lse[0] - np.log(np.arange(1, 41))[None, :])) <= 1e-13
+    inp.q.copy_(q0)
+    _, lse = _oracle_lse(inp)
+    qd, kd, _ = (t.numpy() for t in _decoded(inp))
+    for h in range(2):
+        z00 = inp.scale * math.fsum(qd[0, 0, h, d] * kd[0, 0, 0, d] for d in range(64))
+        assert abs(lse[0, h, 0] - z00) <= 1e-13 * max(1.0, abs(z00))
+
+
+def test_lse_shifts_with_the_scores():
+    """Adding u to every key adds scale <q_i, u> to every score of row i, and
+    so to its log-sum-exp (integer-valued BF16 inputs keep K + u exact)."""
+    g = torch.Generator().manual_seed(13)
+    B, S, H, D = 1, 30, 2, 16
+    q = torch.randint(-3, 4, (B, S, H, D), generator=g).to(torch.bfloat16)
+    k = torch.randint(-3, 4, (B, S, H, D), generator=g).to(torch.bfloat16)
+    v = torch.randn((B, S, H, D), generator=g).to(torch.bfloat16)
+    u = torch.randint(-2, 3, (D,), generator=g).to(torch.bfloat16)
+    a = synth.AttnInputs(q, k, v, "bf16", 0.1, (1.0, 1.0, 1.0))
+    b = synth.AttnInputs(q, (k.float() + u.float()).to(torch.bfloat16), v, "bf16", 0.1, (1.0, 1.0, 1.0))
+    shift = 0.1 * (q.double() @ u.double())  # [B, S, H]
+    _, la = _oracle_lse(a)
+    _, lb = _oracle_lse(b)
+    assert np.max(np.abs(lb - la - shift.permute(0, 2, 1).numpy())) <= 1e-12
+
+
+def test_lse_row_subset_matches_full():
+    inp = synth.make_inputs(B=2, S=37, Hq=4, Hkv=2, Dqk=16, Dv=16, dtype="fp8", seed=14)
+    _, full = _oracle_lse(inp)
+    rows = np.array([(1, 3, 36), (0, 0, 0), (1, 1, 17), (0, 2, 5)], dtype=np.int64)
+    _, sub = _oracle_lse(inp, rows=rows)
+    assert np.array_equal(sub, np.array([full[b, h, i] for b, h, i in rows]))
