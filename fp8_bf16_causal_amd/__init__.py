@@ -1,7 +1,7 @@
 """MI355X (gfx950) causal prefill attention forward: FP8 e4m3 or BF16 inputs,
 BF16 output, through the C-ABI library libfp8_bf16_causal.so.
 
-``attn_fwd`` / ``attn_fwd_ex`` / ``attn_strerror`` are the C entry points
+``attn_fwd`` / ``attn_fwd_ex`` / ``attn_fwd_lse`` / ``attn_quantize_e4m3`` / ``attn_strerror`` are the C entry points
 (device addresses as ints); ``flash_attn_func`` takes torch tensors. PyTorch
 only provides device memory and the stream.
 """
@@ -11,10 +11,10 @@ import math
 
 from . import synth  # noqa: F401
 from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_EXACT_P,
-                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_quantize_e4m3,
+                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_fwd_lse, attn_quantize_e4m3,
                    attn_strerror)
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_quantize_e4m3", "attn_strerror", "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_quantize_e4m3", "attn_strerror", "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
            "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
 
 
@@ -28,12 +28,14 @@ def _raise(code: int):
 
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, descale_k=None, descale_v=None,
-                    out=None, exact_p=False, block_scale=True):
+                    out=None, exact_p=False, block_scale=True, return_lse=False):
     """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
     factors. Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
-    enqueued on the current stream. exact_p=True / block_scale=False select
-    the FP8 softmax ablations (ATTN_FLAG_EXACT_P / ATTN_FLAG_NO_BLOCKSCALE)."""
+    enqueued on the current stream; with return_lse=True, also a float32
+    tensor [B, Hq, S] of each row's log-sum-exp (attn_fwd_lse). exact_p=True /
+    block_scale=False select the FP8 softmax ablations (ATTN_FLAG_EXACT_P /
+    ATTN_FLAG_NO_BLOCKSCALE)."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -65,12 +67,17 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
         ds = tuple(1.0 if x is None else float(x) for x in (descale_q, descale_k, descale_v))
     flags = (ATTN_FLAG_EXACT_P if exact_p else 0) | (0 if block_scale else ATTN_FLAG_NO_BLOCKSCALE)
     stream = torch.cuda.current_stream(q.device).cuda_stream
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
-        rc = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, Dqk, Dv,
-                         1 if causal else 0, float(softmax_scale), dtype, ds, stream, flags)
+        if return_lse:
+            rc = attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
+                              S, Dqk, Dv, 1 if causal else 0, float(softmax_scale), dtype, ds, stream, flags)
+        else:
+            rc = attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, S, Dqk, Dv,
+                             1 if causal else 0, float(softmax_scale), dtype, ds, stream, flags)
     if rc != ATTN_OK:
         _raise(rc)
-    return out
+    return (out, lse) if return_lse else out
 
 
 def quantize_e4m3(x, hadamard=False):

@@ -40,11 +40,12 @@ bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
 }  // namespace
 
-extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S,
-                           int Dqk, int Dv, int causal, float scale, int dtype, const float* descale_qkv,
-                           void* stream, unsigned flags) {
+static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                         int Hkv, int S, int Dqk, int Dv, int causal, float scale, int dtype,
+                         const float* descale_qkv, void* stream, unsigned flags) {
   // ---- ATTN_ERR_INVALID: malformed arguments
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID;
+  if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Dqk <= 0 || Dv <= 0) return ATTN_ERR_INVALID;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
@@ -93,12 +94,27 @@ extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* ou
   const double cd = (double)scale * dq * dk * kLog2e;
   p.c = (float)(cd > 1e-30 ? cd : 1e-30);
   p.dv = dv;
+  p.lse = lse;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the launch check below is ours
   const hipError_t e = dtype == ATTN_FP8_E4M3 ? fbc::launch_attn_fwd_fp8(p, Dqk, (int)flags, (int)grid, st)
                                               : fbc::launch_attn_fwd_bf16(p, Dqk, (int)grid, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
+}
+
+extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S,
+                           int Dqk, int Dv, int causal, float scale, int dtype, const float* descale_qkv,
+                           void* stream, unsigned flags) {
+  return attn_fwd_impl(q, k, v, out, nullptr, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv, stream,
+                       flags);
+}
+
+extern "C" int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                            int Hkv, int S, int Dqk, int Dv, int causal, float scale, int dtype,
+                            const float* descale_qkv, void* stream, unsigned flags) {
+  if (!lse) return ATTN_ERR_INVALID;
+  return attn_fwd_impl(q, k, v, out, lse, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv, stream, flags);
 }
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S,

@@ -64,7 +64,10 @@ struct AttnParams {
   int xcd_group;  // 1: every KV head's workgroups run on one XCD
   float c;        // softmax scale * dq * dk * log2(e) (> 0)
   float dv;       // output dequantisation factor
+  float* lse;     // NULL, or [B][Hq][S]: each row's log-sum-exp of its logits
 };
+
+constexpr float kLn2 = 0.69314718055994531f;
 
 // Workgroup -> (batch, query head, query block). Heaviest (latest) query blocks
 // first, so the causal tail finishes on light work. Workgroups are dispatched

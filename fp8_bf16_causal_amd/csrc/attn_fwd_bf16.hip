@@ -288,6 +288,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
     const float inv = p.dv / l_tot;
+    // log-sum-exp of the row's logits: sum_j 2^(c s_j) = 2^(c m) l
+    if (p.lse != nullptr && g == 0 && qw0 + l32 < S)
+      p.lse[((size_t)b * p.Hq + h) * S + qw0 + l32] = (m * c + __builtin_amdgcn_logf(l_tot)) * kLn2;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll

@@ -459,6 +459,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
     const float inv = p.dv / lacc[0];
+    // log-sum-exp of the row's logits: sum_j 2^(c s_j) = 2^(c m) l
+    if (p.lse != nullptr && g == 0 && qw0 + l32 < S)
+      p.lse[((size_t)b * p.Hq + h) * S + qw0 + l32] = (m * c + __builtin_amdgcn_logf(lacc[0])) * kLn2;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll

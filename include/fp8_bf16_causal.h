@@ -116,6 +116,28 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
                 unsigned flags);
 
 /*
+ * attn_fwd_lse: attn_fwd_ex that also writes each row's log-sum-exp, the
+ * second result a merge of partial attention over key ranges needs (as in a
+ * context-parallel split of the keys: O = sum_r exp(lse_r - lse) O_r with
+ * lse = ln sum_r exp(lse_r)). The pages do not describe this output; it is
+ * read from the online-softmax state every forward kernel keeps (the running
+ * max m and the row sum l):
+ *   lse[(b*Hq + h)*S + i] = ln sum_{j<=i} exp(scale*dq*dk*<q_i, k_j>)
+ *                        ~= ln(2) * (m c + log2 l),  c = scale*dq*dk*log2(e),
+ * where l sums the probabilities the P V product applies: BF16-rounded (within
+ * about 0.004 of the exact value), or, for FP8, the Lean P codes with their
+ * block scales (within ln(1.075) ~ 0.072: the encoding's largest relative
+ * error).
+ *   lse   device pointer to B*Hq*S floats (4-byte aligned), written entirely;
+ *         float32, natural log, layout [B][Hq][S]
+ * Other arguments and errors as attn_fwd_ex; a null or misaligned lse is
+ * ATTN_ERR_INVALID. The output O is bit-identical to attn_fwd_ex's.
+ */
+int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv, int S,
+                 int Dqk, int Dv, int causal, float scale, int dtype, const float* descale_qkv, void* stream,
+                 unsigned flags);
+
+/*
  * attn_quantize_e4m3: the FP8 quantize prologue. Per-tensor e4m3fn
  * quantisation of a BF16 tensor viewed as `rows` rows of `dim` elements,
  * optionally rotating every row by a normalised Hadamard transform first (for

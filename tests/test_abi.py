@@ -25,7 +25,7 @@ def _declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     declared = _declared_functions()
-    assert {"attn_fwd", "attn_fwd_ex", "attn_strerror"} <= set(declared)
+    assert {"attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_quantize_e4m3", "attn_strerror"} <= set(declared)
     for name in declared:
         assert hasattr(lib, name), name
 
@@ -92,3 +92,19 @@ def test_binding_has_no_cpu_path():
 ])
 def test_quantize_argument_checks(args, code):
     assert fbc.attn_quantize_e4m3(*args) == code
+
+
+def _call_lse(lse, ptrs=(P, P, P, P), **kw):
+    a = dict(GOOD)
+    a.update(kw)
+    return fbc.attn_fwd_lse(*ptrs, lse, a["B"], a["Hq"], a["Hkv"], a["S"], a["Dqk"], a["Dv"], a["causal"],
+                            a["scale"], a["dtype"], None, None, 0)
+
+
+@pytest.mark.parametrize("lse,kw,code", [
+    (0, {}, fbc.ATTN_ERR_INVALID), (P + 2, {}, fbc.ATTN_ERR_INVALID),  # null or misaligned lse
+    (P, dict(ptrs=(0, P, P, P)), fbc.ATTN_ERR_INVALID), (P, dict(S=0), fbc.ATTN_ERR_INVALID),
+    (P, dict(causal=0), fbc.ATTN_ERR_UNSUPPORTED), (P, dict(Dqk=64, Dv=64), fbc.ATTN_ERR_UNSUPPORTED),
+])
+def test_lse_entry_point_argument_checks(lse, kw, code):
+    assert _call_lse(lse, **kw) == code

@@ -1,0 +1,126 @@
+"""GPU tests of the per-row log-sum-exp output (attn_fwd_lse, through the C
+ABI) against the fp64 oracle's lse_i = ln sum_{j<=i} exp(z_ij).
+
+Tolerances, from the arithmetic: the kernels report ln2 * (m c + log2 l) with
+l the sum of the probabilities the P V product applies.
+  BF16: each probability is rounded to BF16 (relative error <= 2^-9), so l is
+        within a factor 1 +- 2^-9 of the exact sum: |d lse| <= ln(1 + 2^-9)
+        ~= 0.002, plus fp32 rounding of m c and log2 -> bound 3e-3.
+  FP8:  each Lean P code decodes within 7.5% of its probability (the pages'
+        bound), so |d lse| <= ln(1.075) ~= 0.0723 -> bound 0.075 (exact-P
+        ablation: 1/17 -> ln(18/17) ~= 0.0572 -> 0.06).
+The output O must be bitwise the same as without the extra result.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_bf16_causal_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = {"bf16": 3e-3, "fp8": 0.075}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_bf16_causal_amd._lib as L
+    L.load()
+    torch.cuda.set_device(0)
+
+
+def _run(inp, exact_p=False):
+    import fp8_bf16_causal_amd as fbc
+    dq, dk, dv = inp.descale
+    dev = torch.device("cuda", 0)
+    q, k, v = (t if t.is_cuda else t.to(dev) for t in (inp.q, inp.k, inp.v))
+    ab = dict(exact_p=exact_p) if inp.dtype == "fp8" else {}
+    o1 = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, **ab)
+    o2, lse = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, return_lse=True,
+                                  **ab)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "O changed with the lse output"
+    return o2, lse
+
+
+def _oracle(inp, rows=None):
+    dq, dk, dv = inp.descale
+    dt = oracle.BF16 if inp.dtype == "bf16" else oracle.FP8_E4M3
+    return oracle.attention(synth.raw_codes(inp.q), synth.raw_codes(inp.k), synth.raw_codes(inp.v), dt, inp.scale,
+                            dq, dk, dv, rows=rows, return_lse=True)
+
+
+def _check(got, ref, tol, label):
+    got = np.asarray(got, dtype=np.float64)
+    assert np.all(np.isfinite(got)), f"{label}: non-finite lse"
+    err = np.abs(got - ref)
+    _say(f"{label}: lse max |err| {err.max():.3e} mean {err.mean():.3e} (<= {tol:g})")
+    assert err.max() <= tol, label
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("B,S,Hq,Hkv,Dqk", [(1, 1, 1, 1, 128), (2, 65, 4, 2, 128), (1, 257, 8, 1, 128),
+                                             (1, 1000, 2, 2, 128), (1, 300, 4, 4, 192)])
+def test_lse_whole_tensor(dtype, B, S, Hq, Hkv, Dqk):
+    inp = synth.make_inputs(B=B, S=S, Hq=Hq, Hkv=Hkv, Dqk=Dqk, Dv=128, dtype=dtype, seed=S + Hq)
+    _say(f"case lse {dtype} B={B} S={S} Hq={Hq} Hkv={Hkv} Dqk={Dqk}")
+    _, lse = _run(inp)
+    _, ref = _oracle(inp)
+    _check(lse.cpu().numpy(), ref, LSE_TOL[dtype], f"{dtype} S={S}")
+
+
+def test_lse_fp8_peaked_and_exact_p():
+    inp = synth.make_inputs(B=1, S=640, Hq=4, Hkv=2, Dqk=128, Dv=128, dtype="fp8", seed=21, structure="peaked")
+    _say("case lse fp8 peaked S=640")
+    _, ref = _oracle(inp)
+    _, lse = _run(inp)
+    _check(lse.cpu().numpy(), ref, LSE_TOL["fp8"], "fp8 peaked lean P")
+    _, lse = _run(inp, exact_p=True)
+    _check(lse.cpu().numpy(), ref, 0.06, "fp8 peaked exact P")
+
+
+@pytest.mark.parametrize("name", ["fp8_mha_s32k", "bf16_mha_s32k"])
+def test_lse_full_size_sampled_rows(name):
+    inp = synth.make_config(name, device="cuda")
+    p = inp.shape
+    _say(f"case lse {name} {p}")
+    _, lse = _run(inp)
+    rng = np.random.default_rng(5)
+    rows = np.array([(0, 0, i) for i in range(32)] + [(0, p["Hq"] - 1, p["S"] - 1 - i) for i in range(32)] +
+                    [(0, int(rng.integers(p["Hq"])), int(rng.integers(p["S"]))) for _ in range(128)], dtype=np.int64)
+    _, ref = _oracle(inp, rows=rows)
+    lse = lse.cpu().numpy()
+    got = np.array([lse[b, h, i] for b, h, i in rows])
+    _check(got, ref, LSE_TOL[inp.dtype], f"{name} sampled {len(rows)} rows")
+    assert not np.isnan(lse).any()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_lse_written_entirely(dtype):
+    """Every element of the [B, Hq, S] result is written (NaN prefill), for a
+    length that leaves the last query block partial."""
+    import fp8_bf16_causal_amd as fbc
+    inp = synth.make_inputs(B=2, S=300, Hq=3, Hkv=1, Dqk=128, Dv=128, dtype=dtype, seed=9)
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    out = torch.empty((2, 300, 3, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.full((2, 3, 300 + 64), float("nan"), dtype=torch.float32, device="cuda")
+    dq, dk, dv = inp.descale
+    rc = fbc.attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), 2, 3, 1, 300,
+                          128, 128, 1, inp.scale, fbc.ATTN_BF16 if dtype == "bf16" else fbc.ATTN_FP8_E4M3,
+                          (dq, dk, dv), torch.cuda.current_stream().cuda_stream, 0)
+    torch.cuda.synchronize()
+    assert rc == fbc.ATTN_OK
+    flat = lse.view(-1)
+    assert not torch.isnan(flat[: 2 * 3 * 300]).any()
+    assert torch.isnan(flat[2 * 3 * 300:]).all()  # nothing written past B*Hq*S
