@@ -108,6 +108,95 @@ def time_quant_prologue(steps, warmup):
     return res
 
 
+def _power_file():
+    """The board's socket-power sensor (hwmon power1_input, microwatts), if the
+    driver exposes one."""
+    import glob
+
+    files = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/power1_input"))
+    return files[0] if files else None
+
+
+def energy_study(seconds):
+    """Sustained throughput, board power and energy efficiency of the FP8 and
+    BF16 kernels on Gaussian and peaked operands of the same 32K shape (the
+    pages report that the clock, and so the speed, depends on the operand
+    values). Board power: hwmon power1_input sampled every 5 ms by a reader
+    thread while the launches run (file reads only). Each case first runs for
+    `seconds` untimed, then about `seconds` timed."""
+    import threading
+
+    import torch
+
+    import fp8_bf16_causal_amd as fbc
+    from fp8_bf16_causal_amd import synth
+
+    pf = _power_file()
+
+    def read_w():
+        with open(pf) as f:
+            return int(f.read()) / 1e6
+
+    def sample(stop, out):
+        while not stop.is_set():
+            out.append(read_w())
+            time.sleep(0.005)
+
+    idle = None
+    if pf:
+        vals = []
+        for _ in range(50):
+            vals.append(read_w())
+            time.sleep(0.01)
+        idle = sum(vals) / len(vals)
+    res = {"power_sensor": pf, "idle_W": None if idle is None else round(idle, 1), "cases": []}
+    for name, structure in (("fp8_mha_s32k", "gaussian"), ("fp8_mha_s32k", "peaked"), ("bf16_mha_s32k", "gaussian"),
+                            ("bf16_mha_s32k", "peaked")):
+        inp = synth.make_config(name, device="cuda", structure=structure)
+        p = inp.shape
+        out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
+        dq, dk, dv = inp.descale
+
+        def launch():
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+
+        launch()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        n_warm = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(10):
+                launch()
+            torch.cuda.synchronize()
+            n_warm += 10
+        per = (time.perf_counter() - t0) / n_warm
+        n = max(10, int(seconds / per))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        watts, stop = [], threading.Event()
+        th = threading.Thread(target=sample, args=(stop, watts)) if pf else None
+        if th:
+            th.start()
+        e0.record()
+        for _ in range(n):
+            launch()
+        e1.record()
+        torch.cuda.synchronize()
+        stop.set()
+        if th:
+            th.join()
+        ms = e0.elapsed_time(e1) / n
+        tf = causal_flops(p) / (ms * 1e-3) / 1e12
+        w = sum(watts) / len(watts) if watts else None
+        res["cases"].append({"workload": name, "structure": structure, "launches": 1 + n_warm + n, "timed": n,
+                             "ms": round(ms, 4), "tflops": round(tf, 1),
+                             "board_W": None if w is None else round(w, 1), "power_samples": len(watts),
+                             "tflop_per_J": None if w is None else round(tf / w, 3)})
+        print(json.dumps({"energy_case": res["cases"][-1]}), flush=True)
+        del inp, out
+        torch.cuda.empty_cache()
+    return res
+
+
 def causal_flops(p):
     return float(p["B"]) * p["Hq"] * p["S"] * p["S"] * (p["Dqk"] + p["Dv"])
 
@@ -152,6 +241,9 @@ def main():
     ap.add_argument("--paths", default=",".join(PATHS))
     ap.add_argument("--no-quant", action="store_true", help="skip the FP8 quantize-prologue timing")
     ap.add_argument("--quant-only", action="store_true", help="time only the FP8 quantize prologue")
+    ap.add_argument("--energy", action="store_true",
+                    help="sustained speed, board power and TFLOP/J on Gaussian vs peaked operands (not a bench line)")
+    ap.add_argument("--energy-seconds", type=float, default=4.0, help="untimed and timed seconds per energy case")
     ap.add_argument("--fp8-flags", type=int, default=0,
                     help="ATTN_FLAG_* bits for the FP8 launches (1 exact P, 2 no block scaling): ablations only")
     args = ap.parse_args()
@@ -174,6 +266,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.energy:
+        print(json.dumps({"energy_study": energy_study(args.energy_seconds)}), flush=True)
+        return
     if args.quant_only:
         print(json.dumps({"quantize_prologue": time_quant_prologue(args.steps, min(args.warmup, 20))}), flush=True)
         return
