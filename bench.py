@@ -235,7 +235,7 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=400, help="untimed steps first (the default, about 5 s, lets the clock settle)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=32768, help="rows per path in the CPU-baseline sample (about 15 s of oracle time on 16 cores)")
+    ap.add_argument("--cpu-rows", type=int, default=65536, help="rows per path in the CPU-baseline sample (about 15 s of oracle time on 16 cores)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one plain 256 MiB device-to-device copy (a known byte count for HBM counters)")
     ap.add_argument("--paths", default=",".join(PATHS))
