@@ -21,7 +21,8 @@
 // rotation's block; whole rows hold whole blocks). A wave takes 512
 // consecutive elements per step, each lane 8 (one 16-byte load): index bits
 // 0-2 of an element are in-lane, bits 3.. are lane bits, so the butterflies
-// for bits 0-2 run in registers and the rest across 8 or 16 lanes. Three
+// for bits 0-2 run in registers and the rest across 8 or 16 lanes (DPP
+// moves within 16-lane rows). Three
 // kernels on one stream: clear the amax word, reduce amax (of the rotated
 // values when rotating) with one vector atomic max per workgroup on the float
 // bits, then rotate again, scale and convert (8-byte stores). HBM-bound:
@@ -38,6 +39,36 @@ constexpr int kWaveElems = 512;     // elements per wave per step, 8 per lane
 
 typedef int qv4i __attribute__((ext_vector_type(4)));
 typedef int qv2i __attribute__((ext_vector_type(2)));
+
+// x from lane (lane ^ HL) of the same 16-lane row (HL = 1, 2, 4, 8), by DPP
+// moves: quad permutations for 1 and 2, half-row mirror then quad reversal
+// for 4 ((i ^ 7) ^ 3 = i ^ 4), rotation by 8 for 8.
+template <int HL>
+__device__ inline float lane_xor(float x) {
+  int v = __builtin_bit_cast(int, x);
+  if constexpr (HL == 1) {
+    v = __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);  // quad_perm [1, 0, 3, 2]
+  } else if constexpr (HL == 2) {
+    v = __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);  // quad_perm [2, 3, 0, 1]
+  } else if constexpr (HL == 4) {
+    v = __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    v = __builtin_amdgcn_mov_dpp(v, 0x1B, 0xF, 0xF, true);   // quad_perm [3, 2, 1, 0]
+  } else {
+    static_assert(HL == 8, "lane distances within a 16-lane row");
+    v = __builtin_amdgcn_mov_dpp(v, 0x128, 0xF, 0xF, true);  // row_ror:8
+  }
+  return __builtin_bit_cast(float, v);
+}
+
+// One butterfly stage across lanes at distance HL: the lane whose index bit
+// is clear holds a and gets a + b, its partner holds b and gets a - b; both
+// as one fused multiply-add with +-1, rounded once like the plain sum.
+template <int HL>
+__device__ inline void cross_lane_stage(float v[8], int lane) {
+  const float sgn = (lane & HL) ? -1.0f : 1.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = fmaf(v[i], sgn, lane_xor<HL>(v[i]));
+}
 
 // The 8 elements e0 .. e0+7 of lane `lane` (e0 = 8 * lane within the wave's
 // 512), rotated by the normalised Walsh-Hadamard transform of block N if HAD.
@@ -60,15 +91,11 @@ __device__ inline void load8(const uint16_t* x, int64_t e0, bool valid, int lane
           v[i] = p + q;
           v[i + h] = p - q;
         }
-#pragma unroll
-    for (int hl = 1; hl < N / 8; hl <<= 1) {  // index bits 3..: across lanes
-      const bool upper = (lane & hl) != 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const float partner = __shfl_xor(v[i], hl, 64);
-        v[i] = upper ? partner - v[i] : v[i] + partner;
-      }
-    }
+    // index bits 3..: across lanes (bit 3 + j of the block index is lane bit j)
+    cross_lane_stage<1>(v, lane);
+    cross_lane_stage<2>(v, lane);
+    cross_lane_stage<4>(v, lane);
+    if constexpr (N == 128) cross_lane_stage<8>(v, lane);
     const float norm = N == 128 ? 0.08838834764831845f : 0.125f;  // fp32(1/sqrt(N))
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] *= norm;
