@@ -210,6 +210,13 @@ __device__ inline void buf_load_lds16(rsrc_t r, uint32_t voff, uint8_t* lds_base
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(lds_u8*)lds_base, 16,
                                            (int)voff, 0, 0, 0);
 }
+// The same with the LDS destination as a byte offset into the workgroup's LDS
+// (no generic-pointer conversion, so no null check on the way).
+__device__ inline uint32_t lds_offset(const uint8_t* p) { return (uint32_t)(uintptr_t)(const lds_u8*)p; }
+__device__ inline void buf_load_lds16_at(rsrc_t r, uint32_t voff, uint32_t lds_off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)(uintptr_t)lds_off, 16,
+                                           (int)voff, 0, 0, 0);
+}
 
 // Direct-to-LDS copy of a key tile through a buffer resource whose range ends
 // at the sequence's last row, so rows past it arrive as zeros. Same LDS row
@@ -268,11 +275,12 @@ struct TileLoader {
   // vmcnt wait can count one tile's loads); one without a remainder
   // instruction sends its last to `spare` (1 KiB of LDS nobody reads), from
   // out of range, so it writes zeros there.
-  __device__ void issue_spare(rsrc_t r, uint8_t* lds_tile, uint8_t* spare, int u) const {
+  // lds_tile and spare are LDS byte offsets
+  __device__ void issue_spare(rsrc_t r, uint32_t lds_tile, uint32_t spare, int u) const {
     if (u < kFull)
-      buf_load_lds16(r, off[u], lds_tile + (wave + NW * u) * 1024);
+      buf_load_lds16_at(r, off[u], lds_tile + (uint32_t)(wave + NW * u) * 1024u);
     else
-      buf_load_lds16(r, off[kFull], rem_inst >= 0 ? lds_tile + rem_inst * 1024 : spare);
+      buf_load_lds16_at(r, off[kFull], rem_inst >= 0 ? lds_tile + (uint32_t)rem_inst * 1024u : spare);
   }
 };
 

@@ -182,24 +182,31 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // Tiles t >= n_tiles (past the workgroup's last tile) are loaded too, with
   // an empty range: zeros into a buffer the schedule has already freed, so
   // the loads need no branch.
-  uint8_t* const spare = lds + L::kSpare;
-  auto load_k = [&](int t, int u) {
-    uint8_t* Kl = Kbuf + ring_offset<L::kStages>(t, L::kKTile);
+  // The buffer's LDS offset and the descriptors are computed once per tile;
+  // the returned issuer takes u = 0 .. kKLoads-1 (K) or kVLoads-1 (V).
+  const uint32_t spare = lds_offset(lds) + L::kSpare;
+  const uint32_t kbase = lds_offset(Kbuf), vbase = lds_offset(Vbuf);
+  auto k_tile = [&](int t) {
+    const uint32_t Kl = kbase + ring_offset<L::kStages>(t, L::kKTile);
     const int k0 = t * L::kBK;
     const uint8_t* src = Kg + (size_t)k0 * k_rs;
     const bool live = t < n_tiles;
     const uint32_t bytes = live ? (uint32_t)(S - k0) * k_rs : 0u;  // through the end of key row S - 1's slot
-    if (u < decltype(kld)::kRegs)
-      kld.issue_spare(make_rsrc(src, bytes), Kl, spare, u);
-    else if constexpr (L::kHi)
-      khld.issue_spare(make_rsrc(src + 128, live ? bytes - 128 : 0u), Kl + L::kKLoTile, spare,
-                       u - decltype(kld)::kRegs);
+    const rsrc_t r = make_rsrc(src, bytes);
+    const rsrc_t rh = make_rsrc(src + 128, live ? bytes - 128 : 0u);
+    return [&, Kl, r, rh](int u) {
+      if (u < decltype(kld)::kRegs)
+        kld.issue_spare(r, Kl, spare, u);
+      else if constexpr (L::kHi)
+        khld.issue_spare(rh, Kl + L::kKLoTile, spare, u - decltype(kld)::kRegs);
+    };
   };
-  auto load_v = [&](int t, int u) {
-    uint8_t* Vl = Vbuf + ring_offset<L::kStages>(t, L::kVTile);
+  auto v_tile = [&](int t) {
+    const uint32_t Vl = vbase + ring_offset<L::kStages>(t, L::kVTile);
     const int k0 = t * L::kBK;
     const uint32_t bytes = t < n_tiles ? (uint32_t)(S - k0) * v_rs : 0u;
-    vld.issue_spare(make_rsrc(Vg + (size_t)k0 * v_rs, bytes), Vl, spare, u);
+    const rsrc_t r = make_rsrc(Vg + (size_t)k0 * v_rs, bytes);
+    return [&, Vl, r](int u) { vld.issue_spare(r, Vl, spare, u); };
   };
 
   // V^T operand of O^T = V^T P^T (32x32x64): A lane (dv row i, half g) byte
@@ -405,15 +412,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     if constexpr (L::kHi) khld.init(k_rs, gw, lane, identity);
 #pragma unroll
     for (int u = 0; u < kKLoads; ++u) {
-      load_k(0, u);
-      load_k(1, u);
+      k_tile(0)(u);
+      k_tile(1)(u);
     }
   } else {
     vld.init(v_rs, gw, lane, vkey_fp8);
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
-      load_v(0, u);
-      load_v(1, u);
+      v_tile(0)(u);
+      v_tile(1)(u);
     }
   }
   wait_vmem();
@@ -431,8 +438,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       phase_x(t);                              // slot 2t: X_t
       lds_barrier();
       if (t < n_tiles) {                       // slot 2t + 1: Y_t, loads K_{t+2}
+        const auto ldk = k_tile(t + 2);
         phase_y(t, [&](int u) {
-          if (u < kKLoads) load_k(t + 2, u);
+          if (u < kKLoads) ldk(u);
         });
         wait_vmem_all_but<kKLoads>();          // K_{t+1} (loaded in slot 2t-1), first read in slot 2t+2
       }
@@ -441,8 +449,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
       if (t >= 1) {                            // slot 2t: Y_{t-1}, loads V_{t+1}
+        const auto ldv = v_tile(t + 1);
         phase_y(t - 1, [&](int u) {
-          if (u < kVLoads) load_v(t + 1, u);
+          if (u < kVLoads) ldv(u);
         });
         wait_vmem_all_but<kVLoads>();          // V_t (loaded in slot 2t-2), first read in slot 2t+1
       }
