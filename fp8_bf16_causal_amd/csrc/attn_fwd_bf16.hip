@@ -57,8 +57,13 @@ __device__ inline int vrow_bf16(int k) { return (k & ~15) | ((k & 3) << 2) | ((k
 // two waves of a SIMD alternate between
 //   X_t: O^T += V^T P_{t-1}^T, then S_t^T = K_t Q^T   [matrix cores]
 //   Y_t: mask, maxima, rescale, P_t = 2^((S - m) c) -> BF16, row sum  [vector ALU]
-// In slot 2t the group-1 waves issue direct-to-LDS loads of K_{t+1} and V_t and
-// wait for them before the barrier closing slot 2t+1; double buffers suffice.
+// Each group copies one operand with direct-to-LDS loads issued at the start
+// of its softmax phase: group 1 loads V_t in slot 2t and waits for it before
+// the barrier closing slot 2t+1; group 0 loads K_{t+1} in slot 2t+1 and waits
+// before the barrier closing that slot (K_{t+1} is first read in slot 2t+2).
+// Each load overwrites a buffer last read at least one slot earlier, so double
+// buffers suffice; splitting the loads (and their address arithmetic) between
+// the groups keeps their softmax phases the same length.
 template <int DQK, int BK>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p) {
   using L = Bf16Layout<DQK, BK>;
@@ -96,11 +101,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
     }
   }
 
-  // Only group 1 issues the direct-to-LDS loads, at the start of its softmax
-  // phase (slot 2t), so that no wave starts a matrix phase behind a burst of
-  // its own memory instructions.
+  // Loads are issued at the start of a softmax phase, so that no wave starts
+  // a matrix phase behind a burst of its own memory instructions.
   constexpr int kLoadWaves = kWaves / 2;
-  const int lw = wave - kLoadWaves;
+  const int lw = wave & (kLoadWaves - 1);  // index within the wave's group
   auto identity = [](int r) { return r; };
   auto issue_k = [&](int t) {
     uint8_t* Kl = Kbuf + (t & 1) * L::kKTile;
@@ -261,20 +265,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   lds_barrier();
 
   // One copy of the slot loop per group (2 slots per iteration): same
-  // barriers in the same slots, simpler live ranges. Group 1 stages tiles.
+  // barriers in the same slots, simpler live ranges. Group 0 stages K tiles,
+  // group 1 V tiles.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
       phase_x(t);                              // slot 2t: X_t
       lds_barrier();
-      if (t < wave_tiles) phase_y(t);          // slot 2t + 1: Y_t
+      if (t < n_tiles) {                       // slot 2t + 1: Y_t, loads K_{t+1}
+        if (t + 1 < n_tiles) issue_k(t + 1);
+        if (t < wave_tiles) phase_y(t);
+        wait_vmem();                           // K_{t+1} is first read in slot 2t + 2
+      }
       lds_barrier();
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      if (t < n_tiles) {                       // slot 2t: Y_{t-1}
-        if (t + 1 < n_tiles) issue_k(t + 1);
-        issue_v(t);
-      }
+      if (t < n_tiles) issue_v(t);            // slot 2t: Y_{t-1}, loads V_t
       if (t >= 1 && t - 1 < wave_tiles) phase_y(t - 1);
       lds_barrier();
       phase_x(t);                              // slot 2t + 1: X_t
