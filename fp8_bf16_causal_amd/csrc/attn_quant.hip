@@ -144,16 +144,35 @@ __global__ __launch_bounds__(kQuantThreads) void quant_convert_kernel(const uint
   const float amax = scale[1];
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
+  // y / s correctly rounded, from the correctly rounded reciprocal r = 1/s:
+  // q0 = y r is within one ulp of y / s, the remainder y - s q0 is exact
+  // (one fma), and q0 + r (y - s q0) rounds to the correctly rounded quotient
+  // (Markstein's theorem) as long as nothing underflows, which holds for
+  // s >= 2^-69. Smaller scales take the plain division.
+  const float r = 1.0f / s;
+  const bool fast = s >= 0x1p-69f;
   for (int64_t base = wave * kWaveElems; base < n; base += nwaves * kWaveElems) {
     const int64_t e0 = base + 8 * lane;
     const bool valid = e0 < n;
     float v[8];
     load8<HAD, N>(x, e0, valid, lane, v);
+    float q[8];
+    if (fast) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float q0 = v[i] * r;
+        // (copysign keeps -0: the correction would turn it into +0)
+        q[i] = copysignf(fmaf(fmaf(-q0, s, v[i]), r, q0), v[i]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = v[i] / s;
+    }
     qv2i out;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i] / s, v[4 * i + 1] / s, 0, false);
-      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[4 * i + 2] / s, v[4 * i + 3] / s, w, true);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i], q[4 * i + 1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i + 2], q[4 * i + 3], w, true);
       out[i] = w;
     }
     if (valid) *(qv2i*)(y + e0) = out;

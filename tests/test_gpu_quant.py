@@ -57,6 +57,25 @@ def test_codes_bit_exact(rows, dim, hadamard):
     assert mism == 0, f"{mism} codes differ"
 
 
+@pytest.mark.parametrize("hadamard", [False, True])
+@pytest.mark.parametrize("exp2", [-100, -40, 20])
+def test_codes_bit_exact_at_extreme_scales(hadamard, exp2):
+    """Values spread over many binades, times 2^exp2 (exact in BF16): with
+    2^-100 the scale falls below 2^-69 and the kernel takes its plain-division
+    path, with 2^-40 and 2^20 its reciprocal-and-correction path. The spread
+    leaves many quotients tiny, so subnormal e4m3 codes are exercised."""
+    g = torch.Generator().manual_seed(31 - exp2)
+    x = torch.randn((2000, 128), generator=g) * torch.exp2(torch.randn((2000, 1), generator=g) * 6)
+    x = (x * 2.0 ** exp2).to(torch.bfloat16)
+    _say(f"quantize extreme scale 2^{exp2} hadamard={hadamard}")
+    codes, sc = run_quant(x, hadamard)
+    ref, s, amax = quant.quantize_e4m3(bits(x), hadamard)
+    assert sc[1] == amax and sc[0] == s
+    mism = int(np.sum(codes.reshape(ref.shape) != ref))
+    assert mism == 0, f"{mism} codes differ"
+    assert (ref & 0x7F).min() == 0 and np.sum((ref & 0x7F) < 8) > 1000  # many subnormal codes exercised
+
+
 def test_zero_tensor():
     codes, sc = run_quant(torch.zeros((9, 128), dtype=torch.bfloat16), True)
     assert sc[0] == 1.0 and sc[1] == 0.0 and not codes.any()
