@@ -49,6 +49,9 @@ def _load():
     lib.oracle_attn_lse_f64.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f64, f64, f64, f64, vp, i64,
                                         vp, vp, i32]
     lib.oracle_attn_lse_f64.restype = i32
+    lib.oracle_attn_prefix_f64.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f64, f64, f64, f64,
+                                           vp, i64, vp, vp, i32]
+    lib.oracle_attn_prefix_f64.restype = i32
     lib.oracle_attn_probs_f64.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, f64, f64, f64, i32, i32, vp]
     lib.oracle_attn_probs_f64.restype = i32
     _lib = lib
@@ -83,16 +86,18 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, scale: fl
               dk: float = 1.0, dv: float = 1.0, rows=None, nthreads: int = 0, return_lse: bool = False):
     """Exact causal attention, fp64.
 
-    q [B,S,Hq,Dqk], k [B,S,Hkv,Dqk], v [B,S,Hkv,Dv]: raw codes (uint16 bf16 or
-    uint8 e4m3fn). rows: None (returns [B,S,Hq,Dv]) or an int array [n,3] of
-    (b, h, i) (returns [n,Dv]). With return_lse, also the natural log-sum-exp
-    of each row's logits scale*dq*dk*<q_i, k_j> over j <= i ([B,Hq,S], or [n]).
+    q [B,S,Hq,Dqk], k [B,Sk,Hkv,Dqk], v [B,Sk,Hkv,Dv]: raw codes (uint16 bf16
+    or uint8 e4m3fn), Sk >= S; the queries are the last S positions, so query
+    i sees keys j <= i + Sk - S. rows: None (returns [B,S,Hq,Dv]) or an int
+    array [n,3] of (b, h, i) (returns [n,Dv]). With return_lse, also the
+    natural log-sum-exp of each row's logits scale*dq*dk*<q_i, k_j> over its
+    visible keys ([B,Hq,S], or [n]).
     """
     lib = _load()
     q, k, v = _codes(q, dtype), _codes(k, dtype), _codes(v, dtype)
     B, S, Hq, Dqk = q.shape
-    Hkv, Dv = k.shape[2], v.shape[3]
-    if k.shape != (B, S, Hkv, Dqk) or v.shape != (B, S, Hkv, Dv):
+    Sk, Hkv, Dv = k.shape[1], k.shape[2], v.shape[3]
+    if k.shape != (B, Sk, Hkv, Dqk) or v.shape != (B, Sk, Hkv, Dv) or Sk < S:
         raise ValueError("shape mismatch")
     if rows is None:
         out = np.empty((B, S, Hq, Dv), dtype=np.float64)
@@ -103,11 +108,11 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: int, scale: fl
         out = np.empty((rows.shape[0], Dv), dtype=np.float64)
         lse = np.empty((rows.shape[0],), dtype=np.float64) if return_lse else None
         rp, n = rows.ctypes.data, rows.shape[0]
-    rc = lib.oracle_attn_lse_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, B, Hq, Hkv, S, Dqk, Dv,
-                                 float(scale), float(dq), float(dk), float(dv), rp, n, out.ctypes.data,
-                                 lse.ctypes.data if return_lse else None, int(nthreads))
+    rc = lib.oracle_attn_prefix_f64(q.ctypes.data, k.ctypes.data, v.ctypes.data, dtype, B, Hq, Hkv, S, Sk, Dqk, Dv,
+                                    float(scale), float(dq), float(dk), float(dv), rp, n, out.ctypes.data,
+                                    lse.ctypes.data if return_lse else None, int(nthreads))
     if rc != 0:
-        raise ValueError("oracle_attn_lse_f64 rejected its arguments")
+        raise ValueError("oracle_attn_prefix_f64 rejected its arguments")
     return (out, lse) if return_lse else out
 
 

@@ -76,9 +76,9 @@ static double decode_elem(const void* base, int dtype, size_t idx) {
 typedef struct {
   /* inputs */
   const void *q, *k, *v;
-  int dtype, B, Hq, Hkv, S, Dqk, Dv;
+  int dtype, B, Hq, Hkv, Sq, Sk, Dqk, Dv;
   double score_scale, dv;
-  /* decoded K/V of the KV head being processed: [S][Dqk], [S][Dv] */
+  /* decoded K/V of the KV head being processed: [Sk][Dqk], [Sk][Dv] */
   const double *kd, *vd;
   int b, g;
   /* rows to compute: (h, i) pairs and where each result goes */
@@ -93,14 +93,17 @@ typedef struct {
 } job_t;
 
 /* One output row: the definition of causal softmax attention, in fp64; also
- * the row's log-sum-exp ln sum_j exp(s_j) = m + ln l when lse is not NULL. */
+ * the row's log-sum-exp ln sum_j exp(s_j) = m + ln l when lse is not NULL.
+ * Query i (of Sq) sits at position i + Sk - Sq of the key sequence and sees
+ * keys j <= i + Sk - Sq (with Sq = Sk: j <= i). */
 static void one_row(const job_t* J, int h, int i, double* out, double* lse, double* qrow, double* w) {
   const int Dqk = J->Dqk, Dv = J->Dv;
-  size_t qoff = (((size_t)J->b * J->S + i) * J->Hq + h) * Dqk;
+  const int last = i + (J->Sk - J->Sq); /* the last visible key */
+  size_t qoff = (((size_t)J->b * J->Sq + i) * J->Hq + h) * Dqk;
   for (int d = 0; d < Dqk; ++d) qrow[d] = decode_elem(J->q, J->dtype, qoff + d);
-  /* scores s_j = scale * dq * dk * <q_i, k_j> for visible keys j <= i */
+  /* scores s_j = scale * dq * dk * <q_i, k_j> for visible keys j <= last */
   double m = -INFINITY;
-  for (int j = 0; j <= i; ++j) {
+  for (int j = 0; j <= last; ++j) {
     const double* kr = J->kd + (size_t)j * Dqk;
     double acc = 0.0;
     for (int d = 0; d < Dqk; ++d) acc += qrow[d] * kr[d];
@@ -109,12 +112,12 @@ static void one_row(const job_t* J, int h, int i, double* out, double* lse, doub
   }
   /* softmax weights relative to the row max, and their sum */
   double l = 0.0;
-  for (int j = 0; j <= i; ++j) {
+  for (int j = 0; j <= last; ++j) {
     w[j] = exp(w[j] - m);
     l += w[j];
   }
   for (int d = 0; d < Dv; ++d) out[d] = 0.0;
-  for (int j = 0; j <= i; ++j) {
+  for (int j = 0; j <= last; ++j) {
     const double* vr = J->vd + (size_t)j * Dv;
     const double wj = w[j];
     for (int d = 0; d < Dv; ++d) out[d] += wj * vr[d];
@@ -126,7 +129,7 @@ static void one_row(const job_t* J, int h, int i, double* out, double* lse, doub
 static void* worker(void* arg) {
   job_t* J = (job_t*)arg;
   double* qrow = (double*)malloc(sizeof(double) * (size_t)J->Dqk);
-  double* w = (double*)malloc(sizeof(double) * (size_t)J->S);
+  double* w = (double*)malloc(sizeof(double) * (size_t)J->Sk);
   if (!qrow || !w) {
     free(qrow);
     free(w);
@@ -152,25 +155,28 @@ int oracle_num_threads(int requested) {
 }
 
 /*
- * oracle_attn_lse_f64: exact causal attention on the given inputs, and the
- * natural log-sum-exp of each row's scores (the logits scale*dq*dk*<q_i, k_j>,
- * j <= i). oracle_attn_f64 is the same without the log-sum-exp.
+ * oracle_attn_prefix_f64: exact causal attention of Sq queries over Sk >= Sq
+ * keys, the queries being the last Sq positions (query i sees keys
+ * j <= i + Sk - Sq), and the natural log-sum-exp of each row's logits
+ * scale*dq*dk*<q_i, k_j> over its visible keys. oracle_attn_lse_f64 is the
+ * case Sq = Sk = S, oracle_attn_f64 the same without the log-sum-exp.
  *
- *   q [B][S][Hq][Dqk], k [B][S][Hkv][Dqk], v [B][S][Hkv][Dv]: raw element codes
- *   (uint16 bfloat16 when dtype == 0, uint8 e4m3fn when dtype == 1), host memory.
+ *   q [B][Sq][Hq][Dqk], k [B][Sk][Hkv][Dqk], v [B][Sk][Hkv][Dv]: raw element
+ *   codes (uint16 bfloat16 when dtype == 0, uint8 e4m3fn when dtype == 1), host memory.
  *   scale: softmax scale; dq, dk, dv: per-tensor dequantisation factors (1 for BF16).
- *   rows: NULL for every row, giving out [B][S][Hq][Dv] and lse [B][Hq][S];
+ *   rows: NULL for every row, giving out [B][Sq][Hq][Dv] and lse [B][Hq][Sq];
  *   otherwise nrows triples (b, h, i) with out [nrows][Dv] and lse [nrows].
  *   lse: NULL, or where the log-sum-exps go.
  *   nthreads: worker threads, 0 for every online core.
  * Returns 0, or -1 on invalid arguments / allocation failure.
  */
-int oracle_attn_lse_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int S,
-                        int Dqk, int Dv, double scale, double dq, double dk, double dv, const int64_t* rows,
-                        int64_t nrows, double* out, double* lse, int nthreads) {
+int oracle_attn_prefix_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int Sq,
+                           int Sk, int Dqk, int Dv, double scale, double dq, double dk, double dv,
+                           const int64_t* rows, int64_t nrows, double* out, double* lse, int nthreads) {
+  const int S = Sq;
   if (!q || !k || !v || !out) return -1;
   if (dtype != ORACLE_BF16 && dtype != ORACLE_FP8_E4M3) return -1;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Dqk <= 0 || Dv <= 0 || Hq % Hkv) return -1;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Sk < S || Dqk <= 0 || Dv <= 0 || Hq % Hkv) return -1;
   const int G = Hq / Hkv;
   const int64_t total = rows ? nrows : (int64_t)B * S * Hq;
   if (total < 0) return -1;
@@ -181,8 +187,8 @@ int oracle_attn_lse_f64(const void* q, const void* k, const void* v, int dtype, 
   }
   nthreads = oracle_num_threads(nthreads);
 
-  double* kd = (double*)malloc(sizeof(double) * (size_t)S * Dqk);
-  double* vd = (double*)malloc(sizeof(double) * (size_t)S * Dv);
+  double* kd = (double*)malloc(sizeof(double) * (size_t)Sk * Dqk);
+  double* vd = (double*)malloc(sizeof(double) * (size_t)Sk * Dv);
   int32_t* rh = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total ? total : 1));
   int32_t* ri = (int32_t*)malloc(sizeof(int32_t) * (size_t)(total ? total : 1));
   double** ro = (double**)malloc(sizeof(double*) * (size_t)(total ? total : 1));
@@ -218,14 +224,14 @@ int oracle_attn_lse_f64(const void* q, const void* k, const void* v, int dtype, 
           }
       }
       if (n == 0) continue;
-      for (int j = 0; j < S; ++j) {
-        size_t ko = (((size_t)b * S + j) * Hkv + g) * Dqk, vo = (((size_t)b * S + j) * Hkv + g) * Dv;
+      for (int j = 0; j < Sk; ++j) {
+        size_t ko = (((size_t)b * Sk + j) * Hkv + g) * Dqk, vo = (((size_t)b * Sk + j) * Hkv + g) * Dv;
         for (int d = 0; d < Dqk; ++d) kd[(size_t)j * Dqk + d] = decode_elem(k, dtype, ko + d);
         for (int d = 0; d < Dv; ++d) vd[(size_t)j * Dv + d] = decode_elem(v, dtype, vo + d);
       }
       job_t J;
       memset(&J, 0, sizeof J);
-      J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.S = S;
+      J.q = q; J.k = k; J.v = v; J.dtype = dtype; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Sq = S; J.Sk = Sk;
       J.Dqk = Dqk; J.Dv = Dv; J.score_scale = scale * dq * dk; J.dv = dv;
       J.kd = kd; J.vd = vd; J.b = b; J.g = g;
       J.row_h = rh; J.row_i = ri; J.row_out = ro; J.row_lse = lse ? rl : NULL; J.nrows = n; J.next = 0;
@@ -245,6 +251,13 @@ int oracle_attn_lse_f64(const void* q, const void* k, const void* v, int dtype, 
 done:
   free(kd); free(vd); free(rh); free(ri); free(ro); free(rl); free(th);
   return rc;
+}
+
+int oracle_attn_lse_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int S,
+                        int Dqk, int Dv, double scale, double dq, double dk, double dv, const int64_t* rows,
+                        int64_t nrows, double* out, double* lse, int nthreads) {
+  return oracle_attn_prefix_f64(q, k, v, dtype, B, Hq, Hkv, S, S, Dqk, Dv, scale, dq, dk, dv, rows, nrows, out, lse,
+                                nthreads);
 }
 
 int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int B, int Hq, int Hkv, int S,

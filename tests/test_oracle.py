@@ -294,3 +294,73 @@ def test_lse_row_subset_matches_full():
     rows = np.array([(1, 3, 36), (0, 0, 0), (1, 1, 17), (0, 2, 5)], dtype=np.int64)
     _, sub = _oracle_lse(inp, rows=rows)
     assert np.array_equal(sub, np.array([full[b, h, i] for b, h, i in rows]))
+
+
+# ---------------------------------------------------------------- queries after a key prefix (Sq < Sk)
+
+def _prefix_inputs(dtype, B, Sq, Sk, Hq, Hkv, D, seed):
+    """Queries of the last Sq positions over Sk keys: the key side of a full
+    Sk-long input and the last Sq rows of its queries."""
+    full = synth.make_inputs(B=B, S=Sk, Hq=Hq, Hkv=Hkv, Dqk=D, Dv=D + 2, dtype=dtype, seed=seed)
+    q = full.q[:, Sk - Sq:].contiguous()
+    return full, synth.AttnInputs(q, full.k, full.v, full.dtype, full.scale, full.descale)
+
+
+def _brute_force_prefix(qd, kd, vd, scale):
+    """Materialised attention of Sq queries over Sk keys, query i seeing keys
+    j <= i + Sk - Sq, with math.fsum; returns (out, lse)."""
+    B, Sq, Hq, D = qd.shape
+    Sk, Hkv, Dv = kd.shape[1], kd.shape[2], vd.shape[3]
+    rep, off = Hq // Hkv, Sk - Sq
+    out, lse = np.zeros((B, Sq, Hq, Dv)), np.zeros((B, Hq, Sq))
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Sq):
+                z = [scale * math.fsum(qd[b, i, h, d] * kd[b, j, h // rep, d] for d in range(D)) for j in range(i + off + 1)]
+                top = max(z)
+                ls = top + math.log(math.fsum(math.exp(x - top) for x in z))
+                lse[b, h, i] = ls
+                for d in range(Dv):
+                    out[b, i, h, d] = math.fsum(math.exp(z[j] - ls) * vd[b, j, h // rep, d] for j in range(len(z)))
+    return out, lse
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("Sq,Sk,Hq,Hkv", [(1, 9, 2, 1), (5, 12, 2, 2), (7, 7, 4, 2), (3, 20, 4, 1)])
+def test_prefix_matches_brute_force(dtype, Sq, Sk, Hq, Hkv):
+    _, inp = _prefix_inputs(dtype, 2, Sq, Sk, Hq, Hkv, 6, seed=Sq * 13 + Sk)
+    qd, kd, vd = (t.numpy() for t in _decoded(inp))
+    ref_o, ref_l = _brute_force_prefix(qd, kd, vd, inp.scale)
+    got_o, got_l = _oracle_lse(inp)
+    assert np.max(np.abs(got_o - ref_o)) <= 1e-13 * max(1.0, np.max(np.abs(ref_o)))
+    assert np.max(np.abs(got_l - ref_l)) <= 1e-12
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prefix_matches_sdpa_with_bottom_right_mask(dtype):
+    _, inp = _prefix_inputs(dtype, 1, 40, 100, 4, 2, 32, seed=77)
+    qd, kd, vd = _decoded(inp)
+    mask = torch.ones(40, 100, dtype=torch.bool).tril(diagonal=60)  # key j visible to query i iff j <= i + 60
+    rep = 2
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qd.permute(0, 2, 1, 3), kd.repeat_interleave(rep, dim=2).permute(0, 2, 1, 3),
+        vd.repeat_interleave(rep, dim=2).permute(0, 2, 1, 3), attn_mask=mask, scale=inp.scale).permute(0, 2, 1, 3)
+    assert np.max(np.abs(_oracle(inp) - ref.numpy())) <= 1e-12
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_prefix_equals_the_suffix_of_full_attention(dtype):
+    """Queries after a key prefix give the last rows of full causal attention
+    over the whole sequence (output and log-sum-exp)."""
+    full, inp = _prefix_inputs(dtype, 2, 45, 130, 4, 2, 16, seed=78)
+    fo, fl = _oracle_lse(full)
+    po, pl = _oracle_lse(inp)
+    assert np.array_equal(po, fo[:, 130 - 45:])
+    assert np.array_equal(pl, fl[:, :, 130 - 45:])
+
+
+def test_prefix_rejects_fewer_keys_than_queries():
+    full = synth.make_inputs(B=1, S=8, Hq=1, Hkv=1, Dqk=8, Dv=8, dtype="bf16", seed=1)
+    with pytest.raises(ValueError):
+        oracle.attention(synth.raw_codes(full.q), synth.raw_codes(full.k[:, :5].contiguous()),
+                         synth.raw_codes(full.v[:, :5].contiguous()), oracle.BF16, 0.1)
