@@ -1,7 +1,8 @@
 """MI355X (gfx950) causal prefill attention forward: FP8 e4m3 or BF16 inputs,
 BF16 output, through the C-ABI library libfp8_bf16_causal.so.
 
-``attn_fwd`` / ``attn_fwd_ex`` / ``attn_fwd_lse`` / ``attn_quantize_e4m3`` / ``attn_strerror`` are the C entry points
+``attn_fwd`` / ``attn_fwd_ex`` / ``attn_fwd_lse`` / ``attn_fwd_prefix`` / ``attn_quantize_e4m3`` /
+``attn_strerror`` are the C entry points
 (device addresses as ints); ``flash_attn_func`` takes torch tensors. PyTorch
 only provides device memory and the stream.
 """
@@ -11,10 +12,11 @@ import math
 
 from . import synth  # noqa: F401
 from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_EXACT_P,
-                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_fwd_lse, attn_quantize_e4m3,
+                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_fwd_lse, attn_fwd_prefix,
+                   attn_quantize_e4m3,
                    attn_strerror)
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_quantize_e4m3", "attn_strerror", "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_fwd_prefix", "attn_quantize_e4m3", "attn_strerror", "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
            "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
 
 
@@ -33,7 +35,9 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
     factors. Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
     enqueued on the current stream; with return_lse=True, also a float32
-    tensor [B, Hq, S] of each row's log-sum-exp (attn_fwd_lse). exact_p=True /
+    tensor [B, Hq, S] of each row's log-sum-exp (attn_fwd_lse). k and v may be
+    longer than q (Sk > Sq): the queries are then the last Sq positions and
+    query i sees keys j <= i + Sk - Sq (attn_fwd_prefix). exact_p=True /
     block_scale=False select the FP8 softmax ablations (ATTN_FLAG_EXACT_P /
     ATTN_FLAG_NO_BLOCKSCALE)."""
     import torch
@@ -53,7 +57,8 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     if not (q.is_contiguous() and k.is_contiguous() and v.is_contiguous()):
         raise ValueError("q, k, v must be contiguous")
     B, S, Hq, Dqk = q.shape
-    if k.shape[:2] != (B, S) or v.shape[:3] != k.shape[:3] or k.shape[3] != Dqk:
+    Sk = k.shape[1]
+    if k.shape[0] != B or Sk < S or v.shape[:3] != k.shape[:3] or k.shape[3] != Dqk:
         raise ValueError("shape mismatch between q, k and v")
     Hkv, Dv = k.shape[2], v.shape[3]
     if softmax_scale is None:
@@ -69,7 +74,11 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
-        if return_lse:
+        if Sk != S:
+            rc = attn_fwd_prefix(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr() if return_lse else None, B, Hq, Hkv, S, Sk, Dqk, Dv, 1 if causal else 0,
+                                 float(softmax_scale), dtype, ds, stream, flags)
+        elif return_lse:
             rc = attn_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq, Hkv,
                               S, Dqk, Dv, 1 if causal else 0, float(softmax_scale), dtype, ds, stream, flags)
         else:

@@ -38,6 +38,9 @@ def load():
     lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
                                  ctypes.POINTER(ctypes.c_float), vp, u32]
     lib.attn_fwd_lse.restype = i32
+    lib.attn_fwd_prefix.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
+                                    ctypes.POINTER(ctypes.c_float), vp, u32]
+    lib.attn_fwd_prefix.restype = i32
     lib.attn_quantize_e4m3.argtypes = [vp, vp, vp, ctypes.c_longlong, i32, i32, vp]
     lib.attn_quantize_e4m3.restype = i32
     lib.attn_strerror.argtypes = [i32]
@@ -67,6 +70,17 @@ def attn_fwd_lse(q, k, v, out, lse, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype
     if descale_qkv is not None:
         ds = (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
     return load().attn_fwd_lse(q, k, v, out, lse, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, ds, stream, flags)
+
+
+def attn_fwd_prefix(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, Dqk, Dv, causal, scale, dtype, descale_qkv=None,
+                    stream=None, flags=0) -> int:
+    """Sq queries (the last Sq positions) over Sk >= Sq keys; lse: device
+    address of B*Hq*Sq float32 or None."""
+    ds = None
+    if descale_qkv is not None:
+        ds = (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
+    return load().attn_fwd_prefix(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, Dqk, Dv, causal, scale, dtype, ds, stream,
+                                  flags)
 
 
 def attn_quantize_e4m3(x, y, scale, rows, dim, hadamard, stream=None) -> int:

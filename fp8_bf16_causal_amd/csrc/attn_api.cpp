@@ -40,14 +40,16 @@ bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
 
 }  // namespace
 
+// Sq query rows (the last Sq positions) over Sk >= Sq key rows.
 static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
-                         int Hkv, int S, int Dqk, int Dv, int causal, float scale, int dtype,
+                         int Hkv, int Sq, int Sk, int Dqk, int Dv, int causal, float scale, int dtype,
                          const float* descale_qkv, void* stream, unsigned flags) {
+  const int S = Sq;
   // ---- ATTN_ERR_INVALID: malformed arguments
   if (!q || !k || !v || !out) return ATTN_ERR_INVALID;
   if (lse && ((uintptr_t)lse & 3u)) return ATTN_ERR_INVALID;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return ATTN_ERR_INVALID;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Dqk <= 0 || Dv <= 0) return ATTN_ERR_INVALID;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Sk < S || Dqk <= 0 || Dv <= 0) return ATTN_ERR_INVALID;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
   if (!std::isfinite(scale) || scale < 0.0f) return ATTN_ERR_INVALID;
   float dq = 1.0f, dk = 1.0f, dv = 1.0f;
@@ -60,10 +62,10 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   if ((flags & ~(unsigned)(ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE)) != 0u) return ATTN_ERR_INVALID;
   const int64_t elem = dtype == ATTN_FP8_E4M3 ? 1 : 2;
   const int64_t dmax = Dqk > Dv ? Dqk : Dv;
-  if ((int64_t)B * S * Hq * dmax * 2 > (INT64_C(1) << 62) || (int64_t)B * S * Hq * dmax * elem > (INT64_C(1) << 62))
+  if ((int64_t)B * Sk * Hq * dmax * 2 > (INT64_C(1) << 62) || (int64_t)B * Sk * Hq * dmax * elem > (INT64_C(1) << 62))
     return ATTN_ERR_INVALID;
   // the kernels address one batch entry of each tensor with 32-bit offsets
-  const int64_t per_batch_max = (int64_t)S * (Hq > Hkv ? Hq : Hkv) * dmax * 2;
+  const int64_t per_batch_max = (int64_t)Sk * (Hq > Hkv ? Hq : Hkv) * dmax * 2;
   if (per_batch_max >= (INT64_C(1) << 32)) return ATTN_ERR_INVALID;
   const int64_t nqb = ((int64_t)S + fbc::kBQ - 1) / fbc::kBQ;
   const int64_t grid = (int64_t)B * Hq * nqb;
@@ -86,6 +88,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.S = S;
+  p.Sk = Sk;
   p.G = Hq / Hkv;
   p.nqb = (int)nqb;
   p.xcd_group = ((int64_t)B * Hkv) % fbc::kXcds == 0 ? 1 : 0;
@@ -106,7 +109,7 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
 extern "C" int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S,
                            int Dqk, int Dv, int causal, float scale, int dtype, const float* descale_qkv,
                            void* stream, unsigned flags) {
-  return attn_fwd_impl(q, k, v, out, nullptr, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv, stream,
+  return attn_fwd_impl(q, k, v, out, nullptr, B, Hq, Hkv, S, S, Dqk, Dv, causal, scale, dtype, descale_qkv, stream,
                        flags);
 }
 
@@ -114,7 +117,15 @@ extern "C" int attn_fwd_lse(const void* q, const void* k, const void* v, void* o
                             int Hkv, int S, int Dqk, int Dv, int causal, float scale, int dtype,
                             const float* descale_qkv, void* stream, unsigned flags) {
   if (!lse) return ATTN_ERR_INVALID;
-  return attn_fwd_impl(q, k, v, out, lse, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv, stream, flags);
+  return attn_fwd_impl(q, k, v, out, lse, B, Hq, Hkv, S, S, Dqk, Dv, causal, scale, dtype, descale_qkv, stream,
+                       flags);
+}
+
+extern "C" int attn_fwd_prefix(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq,
+                               int Hkv, int Sq, int Sk, int Dqk, int Dv, int causal, float scale, int dtype,
+                               const float* descale_qkv, void* stream, unsigned flags) {
+  return attn_fwd_impl(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, Dqk, Dv, causal, scale, dtype, descale_qkv, stream,
+                       flags);
 }
 
 extern "C" int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S,

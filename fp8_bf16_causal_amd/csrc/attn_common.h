@@ -58,7 +58,8 @@ struct AttnParams {
   const void* k;
   const void* v;
   void* out;
-  int B, Hq, Hkv, S;
+  int B, Hq, Hkv, S;  // S: query rows
+  int Sk;             // key rows (>= S); query i sits at position i + Sk - S
   int G;          // Hq / Hkv
   int nqb;        // query blocks per head, ceil(S / kBQ)
   int xcd_group;  // 1: every KV head's workgroups run on one XCD

@@ -77,17 +77,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   const int l32 = lane & 31, g = lane >> 5;
   int b, h, qb;
   map_block(p, blockIdx.x, b, h, qb);
-  const int S = p.S;
+  const int S = p.S, Sk = p.Sk, off = Sk - S;  // query i sees keys j <= i + off
   const int kvh = h / p.G;
   const int q0 = qb * kBQ, qw0 = q0 + wave * kQW;
-  const int n_tiles = (min(q0 + kBQ, S) + BK - 1) / BK;
-  const int wave_tiles = qw0 < S ? (min(qw0 + kQW, S) - 1) / BK + 1 : 0;
+  const int n_tiles = (min(q0 + kBQ, S) + off + BK - 1) / BK;
+  const int wave_tiles = qw0 < S ? (min(qw0 + kQW, S) - 1 + off) / BK + 1 : 0;
 
   const uint32_t q_rs = (uint32_t)p.Hq * DQK * 2, k_rs = (uint32_t)p.Hkv * DQK * 2,
                  v_rs = (uint32_t)p.Hkv * L::kDv * 2;
   const uint8_t* Qg = (const uint8_t*)p.q + (size_t)b * S * q_rs + (size_t)h * DQK * 2;
-  const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * S * k_rs + (size_t)kvh * DQK * 2;
-  const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * S * v_rs + (size_t)kvh * L::kDv * 2;
+  const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * Sk * k_rs + (size_t)kvh * DQK * 2;
+  const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * Sk * v_rs + (size_t)kvh * L::kDv * 2;
 
   // Q^T operand: lane (query l32, half g) holds Q[q][16t + 8g .. +7] per step t.
   v8bf qf[DQK / 16];
@@ -108,13 +108,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   auto identity = [](int r) { return r; };
   auto issue_k = [&](int t) {
     uint8_t* Kl = Kbuf + (t & 1) * L::kKTile;
-    load_tile_lds<BK, 17, 16, kLoadWaves>(Kg, k_rs, t * BK, S, Kl, lw, lane, identity);
+    load_tile_lds<BK, 17, 16, kLoadWaves>(Kg, k_rs, t * BK, Sk, Kl, lw, lane, identity);
     if constexpr (L::kHi)
-      load_tile_lds<BK, 9, 8, kLoadWaves>(Kg + 256, k_rs, t * BK, S, Kl + L::kKLoTile, lw, lane, identity);
+      load_tile_lds<BK, 9, 8, kLoadWaves>(Kg + 256, k_rs, t * BK, Sk, Kl + L::kKLoTile, lw, lane, identity);
   };
   auto issue_v = [&](int t) {
     uint8_t* Vl = Vbuf + (t & 1) * L::kVTile;
-    load_tile_lds<BK, 17, 16, kLoadWaves>(Vg, v_rs, t * BK, S, Vl, lw, lane, vrow_bf16);
+    load_tile_lds<BK, 17, 16, kLoadWaves>(Vg, v_rs, t * BK, Sk, Vl, lw, lane, vrow_bf16);
   };
 
   // V^T operand of v_mfma_f32_32x32x16_bf16 via ds_read_b64_tr_b16: lane
@@ -214,8 +214,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   // Y_t: the softmax phase of tile t.
   auto phase_y = [&](int tt) {
     const int k0 = tt * BK;
-    if (k0 + BK - 1 > qw0) {  // the tile crosses this wave's diagonal
-      const int d = qw0 - k0 + l32 - 4 * g;
+    if (k0 + BK - 1 > qw0 + off) {  // the tile crosses this wave's diagonal
+      const int d = qw0 + off - k0 + l32 - 4 * g;
 #pragma unroll
       for (int sb = 0; sb < L::kNsb; ++sb) mask_block_causal(s[sb], d - 32 * sb);
     }

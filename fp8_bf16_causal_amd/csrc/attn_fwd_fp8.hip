@@ -139,16 +139,16 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   const int l32 = lane & 31, g = lane >> 5;
   int b, h, qb;
   map_block(p, blockIdx.x, b, h, qb);
-  const int S = p.S;
+  const int S = p.S, Sk = p.Sk, off = Sk - S;  // query i sees keys j <= i + off
   const int kvh = h / p.G;
   const int q0 = qb * kBQ, qw0 = q0 + wave * kQW;
-  const int n_tiles = (min(q0 + kBQ, S) + L::kBK - 1) / L::kBK;
-  const int wave_tiles = qw0 < S ? (min(qw0 + kQW, S) - 1) / L::kBK + 1 : 0;
+  const int n_tiles = (min(q0 + kBQ, S) + off + L::kBK - 1) / L::kBK;
+  const int wave_tiles = qw0 < S ? (min(qw0 + kQW, S) - 1 + off) / L::kBK + 1 : 0;
 
   const uint32_t q_rs = (uint32_t)p.Hq * DQK, k_rs = (uint32_t)p.Hkv * DQK, v_rs = (uint32_t)p.Hkv * L::kDv;
   const uint8_t* Qg = (const uint8_t*)p.q + (size_t)b * S * q_rs + (size_t)h * DQK;
-  const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * S * k_rs + (size_t)kvh * DQK;
-  const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * S * v_rs + (size_t)kvh * L::kDv;
+  const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * Sk * k_rs + (size_t)kvh * DQK;
+  const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * Sk * v_rs + (size_t)kvh * L::kDv;
 
   // Q^T operand of S^T = K Q^T: lane (query l32, half g) holds, per 64-wide
   // step t, Q[q][64t + 16g .. +15] and Q[q][64t + 32 + 16g .. +15].
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     const int k0 = t * L::kBK;
     const uint8_t* src = Kg + (size_t)k0 * k_rs;
     const bool live = t < n_tiles;
-    const uint32_t bytes = live ? (uint32_t)(S - k0) * k_rs : 0u;  // through the end of key row S - 1's slot
+    const uint32_t bytes = live ? (uint32_t)(Sk - k0) * k_rs : 0u;  // through the end of key row Sk - 1's slot
     const rsrc_t r = make_rsrc(src, bytes);
     const rsrc_t rh = make_rsrc(src + 128, live ? bytes - 128 : 0u);
     return [&, Kl, r, rh](int u) {
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   auto v_tile = [&](int t) {
     const uint32_t Vl = vbase + ring_offset<L::kStages>(t, L::kVTile);
     const int k0 = t * L::kBK;
-    const uint32_t bytes = t < n_tiles ? (uint32_t)(S - k0) * v_rs : 0u;
+    const uint32_t bytes = t < n_tiles ? (uint32_t)(Sk - k0) * v_rs : 0u;
     const rsrc_t r = make_rsrc(Vg + (size_t)k0 * v_rs, bytes);
     return [&, Vl, r](int u) { vld.issue_spare(r, Vl, spare, u); };
   };
@@ -324,8 +324,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
 #pragma unroll
     for (int u = 0; u < 8; ++u) ld(u);  // this slot's tile loads, first
     __builtin_amdgcn_sched_barrier(0);
-    if (k0 + L::kBK - 1 > qw0) {  // the tile crosses this wave's diagonal (or lies past it)
-      const int d = qw0 - k0 + l32 - 4 * g;
+    if (k0 + L::kBK - 1 > qw0 + off) {  // the tile crosses this wave's diagonal (or lies past it)
+      const int d = qw0 + off - k0 + l32 - 4 * g;
 #pragma unroll
       for (int sb = 0; sb < 4; ++sb) mask_block_causal(s[sb], d - 32 * sb);
     }

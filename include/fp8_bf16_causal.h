@@ -138,6 +138,26 @@ int attn_fwd_lse(const void* q, const void* k, const void* v, void* out, float* 
                  unsigned flags);
 
 /*
+ * attn_fwd_prefix: Sq queries after a prefix of keys. The queries are the last
+ * Sq positions of a sequence of Sk >= Sq keys: query i sits at position
+ * i + Sk - Sq and sees keys j <= i + Sk - Sq (flash_attn_func's causal
+ * alignment when the key sequence is longer, bottom-right). With Sq = Sk this
+ * is attn_fwd_lse (or attn_fwd_ex when lse is NULL). Together with the
+ * log-sum-exp it lets a caller split the keys of one query block into ranges
+ * and merge the partial results (context parallelism). The pages do not
+ * describe this case; it reuses the same kernels with the diagonal moved by
+ * Sk - Sq.
+ *   q     B*Sq*Hq*Dqk elements, layout [B][Sq][Hq][Dqk]
+ *   k, v  [B][Sk][Hkv][Dqk], [B][Sk][Hkv][Dv]
+ *   out   [B][Sq][Hq][Dv] BF16, written entirely
+ *   lse   NULL, or B*Hq*Sq floats ([B][Hq][Sq], 4-byte aligned)
+ * Other arguments and errors as attn_fwd_ex; Sk < Sq is ATTN_ERR_INVALID.
+ */
+int attn_fwd_prefix(const void* q, const void* k, const void* v, void* out, float* lse, int B, int Hq, int Hkv,
+                    int Sq, int Sk, int Dqk, int Dv, int causal, float scale, int dtype, const float* descale_qkv,
+                    void* stream, unsigned flags);
+
+/*
  * attn_quantize_e4m3: the FP8 quantize prologue. Per-tensor e4m3fn
  * quantisation of a BF16 tensor viewed as `rows` rows of `dim` elements,
  * optionally rotating every row by a normalised Hadamard transform first (for

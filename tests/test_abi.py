@@ -108,3 +108,13 @@ def _call_lse(lse, ptrs=(P, P, P, P), **kw):
 ])
 def test_lse_entry_point_argument_checks(lse, kw, code):
     assert _call_lse(lse, **kw) == code
+
+
+@pytest.mark.parametrize("Sq,Sk,lse,code", [
+    (128, 100, P, fbc.ATTN_ERR_INVALID),   # fewer keys than queries
+    (0, 100, P, fbc.ATTN_ERR_INVALID), (128, 256, P + 2, fbc.ATTN_ERR_INVALID),
+])
+def test_prefix_entry_point_argument_checks(Sq, Sk, lse, code):
+    a = dict(GOOD)
+    assert fbc.attn_fwd_prefix(P, P, P, P, lse, a["B"], a["Hq"], a["Hkv"], Sq, Sk, a["Dqk"], a["Dv"], a["causal"],
+                               a["scale"], a["dtype"], None, None, 0) == code
