@@ -10,7 +10,7 @@ matrix, two matrix products of 2 flop per multiply-add); the figure under the
 literal 2*B*H*S^2*(Dqk+Dv) formula is printed beside it. Peaks are MI355X's
 published dense matrix-core figures: 5.0 PFLOP/s FP8, 2.5 PFLOP/s BF16.
 
-Prints one JSON line. --gpus above 1 is refused: this build runs on one GPU.
+Prints one JSON line. --gpus above 1 is refused: the benchmark runs on one GPU.
 """
 from __future__ import annotations
 
@@ -248,7 +248,7 @@ def main():
                     help="ATTN_FLAG_* bits for the FP8 launches (1 exact P, 2 no block scaling): ablations only")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU only (no multi-GPU path); use --gpus 1", file=sys.stderr)
+        print("bench.py: runs on one GPU only (there is no multi-GPU path); use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

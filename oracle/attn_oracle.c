@@ -15,7 +15,7 @@
  *   FAQ -- causal forward only, FP8 e4m3 and BF16, flash_attn_func-compatible
  *   interface.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   - layout is flash_attn_func's (batch, seq, heads, dim), contiguous;
  *   - grouped-query attention: query head h reads KV head h / (Hq / Hkv);
  *   - causal mask with equal query and key lengths: key j is visible to row i

@@ -23,7 +23,7 @@ softmax so that each can be pinned on its own:
    sum of the already-rounded (scaled back) probabilities, so the weights sum
    to one.  [same sections; abstract technique (3).]
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 * x is log2 of the probability relative to the running row max, natural-exp
   softmax being 2**(z*log2(e)).
 * C = 55.63 code units (LEANP_C).  The pages give no value; this is the
