@@ -352,17 +352,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     // encoded probabilities stay in [0, 1]: the plain FP8 softmax.)
     constexpr float kLazy = kBlockScale ? kLazyLog2 : 0.0f;
     const float mt = fmaxf(ma, mb);
-    const float mn = (mt - m) * c > kLazy ? mt : m;
-    const float alpha = (m == mn) ? 1.0f : __builtin_amdgcn_exp2f((m - mn) * c);
-    m = mn;
-    // rescale the accumulators when the running max rose
-    if (__any(alpha != 1.0f)) {
+    const bool rises = (mt - m) * c > kLazy;
+    // move the reference and rescale the accumulators when it rises (rare:
+    // the factor and its exponential are computed only then)
+    if (__any(rises)) {
       // keep this a real branch: the multiplies are skipped on most tiles
       asm volatile("" ::: "memory");
+      const float mn = rises ? mt : m;
+      const float alpha = rises ? __builtin_amdgcn_exp2f((m - mn) * c) : 1.0f;
+      m = mn;
 #pragma unroll
       for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
       lacc *= alpha;
     }
+    const float mn = m;
     // block exponents: the block max lands in (2^7, 2^8]
     const float ka = kBlockScale ? fminf(fmaxf(floorf(8.0f - (ma - mn) * c), 0.0f), 127.0f) : 0.0f;
     const float kb = kBlockScale ? fminf(fmaxf(floorf(8.0f - (mb - mn) * c), 0.0f), 127.0f) : 0.0f;
