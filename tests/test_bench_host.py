@@ -1,0 +1,42 @@
+"""Host-side logic of bench.py (no GPU): the refusal of several GPUs, the
+FLOP convention, the peaks, and how committed profile figures are matched to
+the current kernel sources."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_before_touching_the_device():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_causal_flop_count_and_peaks():
+    p = dict(B=1, Hq=32, S=32768, Dqk=128, Dv=128)
+    # the visible half of the score matrix: B * H * S^2 * (Dqk + Dv)
+    assert bench.causal_flops(p) == 8.796093022208e12
+    # 256 CUs x 4 SIMDs x {2048, 1024} dense flop per clock x 2.4 GHz
+    assert bench.PEAK["fp8"] == pytest.approx(256 * 4 * 2048 * 2.4e9 / 1e12, abs=0.1)
+    assert bench.PEAK["bf16"] == pytest.approx(256 * 4 * 1024 * 2.4e9 / 1e12, abs=0.1)
+
+
+def test_profile_lines_count_only_for_the_current_sources(tmp_path, monkeypatch):
+    sha = bench.sources_sha256("fp8")
+    assert sha == bench.sources_sha256("fp8") and len(sha) == 64
+    f = tmp_path / "traffic.txt"
+    f.write_text("# comment\n"
+                 f"workload=fp8_mha_s32k kernel=k sources_sha256={'0' * 64} traffic_bytes=1\n"
+                 f"workload=fp8_mha_s32k kernel=k sources_sha256={sha} traffic_bytes=1234\n"
+                 f"workload=bf16_mha_s32k kernel=k sources_sha256={sha} traffic_bytes=99\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.measured_traffic("fp8_mha_s32k", "fp8") == 1234
+    # a line taken on other sources (another hash) is not reported
+    assert bench.measured_traffic("bf16_mha_s32k", "bf16") is None
+    assert bench.profiled_line(str(tmp_path / "missing.txt"), "fp8_mha_s32k", "fp8") is None
