@@ -111,13 +111,20 @@ __global__ __launch_bounds__(kQuantThreads) void quant_amax_kernel(const uint16_
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * (kQuantThreads / 64);
+  // four 512-element chunks per wave and step: four independent 16-byte
+  // loads in flight per lane (this pass runs on a small grid)
   float m = 0.0f;
-  for (int64_t base = wave * kWaveElems; base < n; base += nwaves * kWaveElems) {
-    const int64_t e0 = base + 8 * lane;
-    float v[8];
-    load8<HAD, N>(x, e0, e0 < n, lane, v);
+  for (int64_t base = wave * 4 * kWaveElems; base < n; base += nwaves * 4 * kWaveElems) {
+    float v[4][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[i]));
+    for (int j = 0; j < 4; ++j) {
+      const int64_t e0 = base + j * kWaveElems + 8 * lane;
+      load8<HAD, N>(x, e0, e0 < n, lane, v[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(v[j][i]));
   }
 #pragma unroll
   for (int h = 32; h >= 1; h >>= 1) m = fmaxf(m, __shfl_xor(m, h, 64));
