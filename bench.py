@@ -108,6 +108,86 @@ def time_quant_prologue(steps, warmup):
     return res
 
 
+# One GPU's share of each workload under 8-way tensor parallelism over heads
+# (each GPU takes 1/8 of the KV heads with their query heads; no exchange).
+TP_SHARES = [("fp8_mha_s32k", dict(Hq=4, Hkv=4)), ("bf16_mha_s32k", dict(Hq=4, Hkv=4)),
+             ("fp8_gqa_s16k_peaked", dict(Hq=4, Hkv=1)), ("fp8_mla_s32k", dict(Hq=2, Hkv=2))]
+N_CU, N_XCD, BQ, BK = 256, 8, 256, 128
+
+
+def balance_bound(B, Hq, Hkv, S):
+    """Upper bound on the fraction of the chip a causal grid can keep busy:
+    mean CU load / largest CU load when the workgroups, in launch order, go
+    round-robin to the 8 XCDs and, within one, each to the CU that frees
+    first (one workgroup per CU at a time). A workgroup's load is its number
+    of 128-key tiles. The launch order is the kernels' own: heaviest query
+    blocks first over all heads, or, when B*Hkv is a multiple of 8, one KV
+    head's blocks per XCD, heaviest first."""
+    import heapq
+
+    nqb = (S + BQ - 1) // BQ
+    G = Hq // Hkv
+    nkv = B * Hkv
+
+    def tiles(qb):
+        return (min(qb * BQ + BQ, S) + BK - 1) // BK
+
+    order = []
+    if nkv % N_XCD == 0:
+        per_head = G * nqb
+        for bid in range(B * Hq * nqb):
+            slot = bid // N_XCD
+            order.append(tiles(nqb - 1 - (slot % per_head) // G))
+    else:
+        for bid in range(B * Hq * nqb):
+            order.append(tiles(nqb - 1 - bid // (nkv * G)))
+    cus = [[0] * (N_CU // N_XCD) for _ in range(N_XCD)]
+    for bid, w in enumerate(order):
+        heap = cus[bid % N_XCD]
+        heapq.heapreplace(heap, heap[0] + w)
+    total = sum(order)
+    return total / N_CU / max(max(h) for h in cus)
+
+
+def time_tp_shares(full_paths, steps=20, warmup=20):
+    """The kernels at one GPU's share of each workload under 8-way tensor
+    parallelism (1/8 of the heads): small grids, where the causal imbalance
+    between query blocks decides how much of the chip stays busy."""
+    import torch
+
+    import fp8_bf16_causal_amd as fbc
+    from fp8_bf16_causal_amd import synth
+
+    res = []
+    for name, ov in TP_SHARES:
+        inp = synth.make_config(name, device="cuda", **ov)
+        p = inp.shape
+        out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
+        dq, dk, dv = inp.descale
+        for _ in range(warmup):
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[steps // 2]
+        tf = causal_flops(p) / (ms * 1e-3) / 1e12
+        nwg = p["B"] * p["Hq"] * ((p["S"] + BQ - 1) // BQ)
+        row = {"workload": name, "share": "1/8 of the heads", "B": p["B"], "Hq": p["Hq"], "Hkv": p["Hkv"],
+               "S": p["S"], "Dqk": p["Dqk"], "workgroups": nwg, "kernel_ms_median": round(ms, 4),
+               "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK[inp.dtype], 4),
+               "balance_bound": round(balance_bound(p["B"], p["Hq"], p["Hkv"], p["S"]), 4)}
+        if name in full_paths:
+            row["vs_full_shape"] = round(tf / full_paths[name]["tflops"], 4)
+        res.append(row)
+        del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def _power_file():
     """The board's socket-power sensor (hwmon power1_input, microwatts), if the
     driver exposes one."""
@@ -244,6 +324,8 @@ def main():
     ap.add_argument("--energy", action="store_true",
                     help="sustained speed, board power and TFLOP/J on Gaussian vs peaked operands (not a bench line)")
     ap.add_argument("--energy-seconds", type=float, default=4.0, help="untimed and timed seconds per energy case")
+    ap.add_argument("--no-shares", action="store_true",
+                    help="skip the timing of one GPU's share under 8-way tensor parallelism")
     ap.add_argument("--fp8-flags", type=int, default=0,
                     help="ATTN_FLAG_* bits for the FP8 launches (1 exact P, 2 no block scaling): ablations only")
     args = ap.parse_args()
@@ -350,6 +432,8 @@ def main():
             "paths": paths, "roofline": roofline}
     if args.fp8_flags:
         line["fp8_flags"] = args.fp8_flags
+    if not args.no_shares and not args.fp8_flags:
+        line["tp8_shares"] = time_tp_shares(paths)
     if not args.no_quant and not args.fp8_flags:
         line["quantize_prologue"] = time_quant_prologue(20, 5)
     if not args.no_cpu_baseline:

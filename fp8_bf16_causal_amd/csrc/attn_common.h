@@ -112,6 +112,15 @@ __device__ inline float max_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
   return fmaxf(as_f(r[0]), as_f(r[1]));
 }
+// The maxima over lanes l and l ^ 32 of two values at once: two swaps of
+// lane halves instead of two per value.
+__device__ inline void max_xor32_pair(float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(as_u(a), as_u(b), false, false);
+  const float t = fmaxf(as_f(r[0]), as_f(r[1]));  // lanes 0-31: max of a, lanes 32-63: max of b
+  const auto u = __builtin_amdgcn_permlane32_swap(as_u(t), as_u(t), false, false);
+  a = as_f(u[0]);
+  b = as_f(u[1]);
+}
 __device__ inline float sum_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
   return as_f(r[0]) + as_f(r[1]);

@@ -330,19 +330,17 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       for (int sb = 0; sb < 4; ++sb) mask_block_causal(s[sb], d - 32 * sb);
     }
     // per-(row, 64-key block) maxima and the running max
-    float ma = s[0][0], mb = s[2][0];
+    // (four independent chains, one per 32x32 block)
+    float ma0 = s[0][0], ma1 = s[1][0], mb0 = s[2][0], mb1 = s[3][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) {
-      ma = fmaxf(ma, s[0][r]);
-      mb = fmaxf(mb, s[2][r]);
+      ma0 = fmaxf(ma0, s[0][r]);
+      ma1 = fmaxf(ma1, s[1][r]);
+      mb0 = fmaxf(mb0, s[2][r]);
+      mb1 = fmaxf(mb1, s[3][r]);
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      ma = fmaxf(ma, s[1][r]);
-      mb = fmaxf(mb, s[3][r]);
-    }
-    ma = max_xor32(ma);
-    mb = max_xor32(mb);
+    float ma = fmaxf(ma0, ma1), mb = fmaxf(mb0, mb1);
+    max_xor32_pair(ma, mb);
     // Lazy running max: the reference m moves (and the accumulators are
     // rescaled) only when the tile max exceeds it by more than kLazyLog2
     // binades; otherwise probabilities up to 2^kLazyLog2 are encoded relative

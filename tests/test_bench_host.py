@@ -40,3 +40,17 @@ def test_profile_lines_count_only_for_the_current_sources(tmp_path, monkeypatch)
     # a line taken on other sources (another hash) is not reported
     assert bench.measured_traffic("bf16_mha_s32k", "bf16") is None
     assert bench.profiled_line(str(tmp_path / "missing.txt"), "fp8_mha_s32k", "fp8") is None
+
+
+def test_balance_bound_of_causal_grids():
+    # one workgroup per CU: 4 query heads x 64 blocks of 256 rows at S = 16K;
+    # block qb covers 2 qb + 2 key tiles, so the largest load is 128 tiles and
+    # the mean 4 * sum(2 qb + 2) / 256 = 65
+    assert bench.balance_bound(1, 4, 1, 16384) == pytest.approx(65 / 128)
+    # a grid smaller than the chip leaves CUs idle: 2 heads x 1 block
+    assert bench.balance_bound(1, 2, 2, 256) == pytest.approx(2 * 2 / 256 / 2)
+    # many workgroups, heaviest first, balance well; the bound never exceeds 1
+    for B, Hq, Hkv, S in ((1, 32, 32, 32768), (1, 32, 8, 16384), (1, 4, 4, 32768), (2, 6, 3, 5000)):
+        b = bench.balance_bound(B, Hq, Hkv, S)
+        assert 0 < b <= 1
+    assert bench.balance_bound(1, 4, 4, 32768) > 0.98
