@@ -72,8 +72,13 @@ struct Fp8Layout {
   static constexpr int kStages = 3;                   // buffers per operand
   static constexpr int kSpare = kStages * (kKTile + kVTile);  // 1 KiB target of idle loads
   static constexpr int kLoop = kSpare + 1024;
+  // head dim 192: Q's first 64 columns (fragment 0) wait in LDS between the
+  // Q K^T phases, 2 KiB per wave (the registers are short at this width)
+  static constexpr bool kQ0Lds = kHi;
+  static constexpr int kQ0 = kLoop;
+  static constexpr int kLoopQ = kLoop + (kQ0Lds ? kWaves * 2048 : 0);
   static constexpr int kEpi = kWaves * kQW * kOStride;
-  static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
+  static constexpr int kLds = kLoopQ > kEpi ? kLoopQ : kEpi;
 };
 
 // V's LDS row for key k of the tile: the low four bits b3 b2 b1 b0 of k
@@ -105,9 +110,15 @@ __device__ inline int vkey_fp8(int r) {
 // instruction stream because the hardware does not track MFMA completion.]
 //
 // Within X_t the operand fragments are read from LDS two MFMA steps ahead in
-// one ring that runs from the P V steps into the Q K steps; the first two V
-// fragments are read at the end of Y_{t-1}, so the matrix cores start at the
-// barrier.
+// one ring that runs from the P V steps into the Q K steps (K one step ahead
+// at head dim 192); the first two V fragments are read at the end of Y_{t-1},
+// so the matrix cores start at the barrier. Each tile's row sums come from
+// matrix instructions against a ones operand into S's last block, which is
+// free until the fourth Q K step; one register of the result joins the
+// running sum l. At head dim 192 the first Q fragment waits in LDS between
+// tiles. Both keep the registers within budget: a spilled register is
+// reloaded through the vector-memory counter, and that wait would also cover
+// the tile copies still in flight.
 //
 // K/V staging (three buffers per operand): each group copies one operand with
 // direct-to-LDS instructions issued together at the start of its softmax
@@ -166,6 +177,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       qf[t] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
   }
+  uint8_t* const q0l = lds + L::kQ0 + wave * 2048 + 16 * lane;  // this lane's fragment-0 slot (head dim 192)
+  if constexpr (L::kQ0Lds) {
+    *(v4i*)q0l = (v4i){qf[0][0], qf[0][1], qf[0][2], qf[0][3]};
+    *(v4i*)(q0l + 1024) = (v4i){qf[0][4], qf[0][5], qf[0][6], qf[0][7]};
+  }
+  auto q_frag0 = [&]() {
+    if constexpr (L::kQ0Lds) {
+      const v4i lo = ld_lds16(q0l), hi = ld_lds16(q0l + 1024);
+      return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    } else {
+      return qf[0];
+    }
+  };
 
   // Each tile goes through a buffer resource that starts at its first key and
   // ends with key S - 1: rows past the sequence arrive as zeros (finite
@@ -244,13 +268,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   };
 
   // O^T in four 32x32 blocks (lane (query l32, g), register r: dv row
-  // 32 dvb + 8 (r/4) + 4 g + r%4); every register of lacc holds the query's
-  // rounded row sum.
+  // 32 dvb + 8 (r/4) + 4 g + r%4). l: the query's running sum of the rounded
+  // probabilities (each tile's sum comes from a matrix instruction against a
+  // ones operand, every register of whose result holds it; only register 0 is
+  // kept).
   v16f oacc[4];
-  v16f lacc;
+  float l = 0.0f;
 #pragma unroll
   for (int d = 0; d < 4; ++d) oacc[d] = (v16f){};
-  lacc = (v16f){};
   float m = -INFINITY;  // running max of the raw scores of query qw0 + l32
   // the base-2 score scale lives in a vector register: as a scalar it would be
   // spilled and reloaded every tile under this kernel's scalar-register pressure
@@ -281,7 +306,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     // asm definition, no instruction) so it does not occupy registers
     // through the P V half of this phase.
     asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
-    v8i kf[3];
+    // Q K fragments are read kKA steps ahead (one at head dim 192, where the
+    // registers are short)
+    constexpr int kKA = DQK == 128 ? 2 : 1;
+    constexpr int kKR = kKA + 1;
+    v8i kf[kKR];
+    v8i q0;  // Q fragment 0 for the Q K steps
+    // this tile's row sums go through S's block 3, free until Q K step 3
     if (do_pv) {
       const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
@@ -291,28 +322,32 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ks = i >> 2, dvb = i & 3;
-        if (i + 2 < 8)
-          vf[(i + 2) % 3] = read_v(Vl, i + 2);
-        else
-          kf[i - 6] = read_k(Kl, i - 6);  // the first two Q K steps
+        if (i + 2 < 8) vf[(i + 2) % 3] = read_v(Vl, i + 2);
+        if (i >= 8 - kKA) kf[i - (8 - kKA)] = read_k(Kl, i - (8 - kKA));  // the first Q K steps
+        if (i == 7) q0 = q_frag0();
         oacc[dvb] = mfma_32x32x64_fp8(vf[i % 3], P[ks], oacc[dvb], 127, sc[ks]);
         __builtin_amdgcn_sched_barrier(0);
         if (dvb == 3) {
-          lacc = mfma_32x32x64_fp8(ones, P[ks], lacc, 127, sc[ks]);
+          s[3] = mfma_32x32x64_fp8(ones, P[ks], ks == 0 ? (v16f){} : s[3], 127, sc[ks]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     } else {
-      kf[0] = read_k(Kl, 0);
-      kf[1] = read_k(Kl, 1);
+#pragma unroll
+      for (int j = 0; j < kKA; ++j) kf[j] = read_k(Kl, j);
+      q0 = q_frag0();
+      s[3] = (v16f){};
     }
     if (do_qk) {
 #pragma unroll
       for (int i = 0; i < kQkSteps; ++i) {
-        if (i + 2 < kQkSteps) kf[(i + 2) % 3] = read_k(Kl, i + 2);
-        s[i & 3] = mfma_32x32x64_fp8(kf[i % 3], qf[i >> 2], i < 4 ? (v16f){} : s[i & 3], 127, 127);
+        if (i + kKA < kQkSteps) kf[(i + kKA) % kKR] = read_k(Kl, i + kKA);
+        if (i == 3) l += s[3][0];  // three steps after the row-sum instruction
+        s[i & 3] = mfma_32x32x64_fp8(kf[i % kKR], i < 4 ? q0 : qf[i >> 2], i < 4 ? (v16f){} : s[i & 3], 127, 127);
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+      l += s[3][0];
     }
     __builtin_amdgcn_s_setprio(0);
   };
@@ -361,7 +396,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       m = mn;
 #pragma unroll
       for (int d = 0; d < 4; ++d) oacc[d] *= alpha;
-      lacc *= alpha;
+      l *= alpha;
     }
     const float mn = m;
     // block exponents: the block max lands in (2^7, 2^8]
@@ -468,10 +503,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // ---- epilogue: O / l * dv -> BF16, staged through LDS for coalesced rows.
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
-    const float inv = p.dv / lacc[0];
+    const float inv = p.dv / l;
     // log-sum-exp of the row's logits: sum_j 2^(c s_j) = 2^(c m) l
     if (p.lse != nullptr && g == 0 && qw0 + l32 < S)
-      p.lse[((size_t)b * p.Hq + h) * S + qw0 + l32] = (m * c + __builtin_amdgcn_logf(lacc[0])) * kLn2;
+      p.lse[((size_t)b * p.Hq + h) * S + qw0 + l32] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;
 #pragma unroll
     for (int d = 0; d < 4; ++d)
 #pragma unroll
