@@ -103,6 +103,9 @@ __device__ inline v4f mfma_16x16x128_fp8(v8i a, v8i b, v4f c, int scale_a, int s
 __device__ inline v16f mfma_32x32x16_bf16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ inline v4f mfma_16x16x32_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 __device__ inline float as_f(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ inline uint32_t as_u(float f) { return __builtin_bit_cast(uint32_t, f); }
@@ -121,11 +124,6 @@ __device__ inline void max_xor32_pair(float& a, float& b) {
   a = as_f(u[0]);
   b = as_f(u[1]);
 }
-__device__ inline float sum_xor32(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(as_u(x), as_u(x), false, false);
-  return as_f(r[0]) + as_f(r[1]);
-}
-
 // Causal mask of one 32x32 block of S^T (32 keys x 32 queries, accumulator
 // layout): register r of lane (query l32, half g) holds key 8 (r/4) + 4 g +
 // r%4 of the block. With d = (query - first key of the block) - 4 g, that key

@@ -15,8 +15,9 @@
 // of BK keys staged in LDS by direct-to-LDS loads, double-buffered, with the
 // same two-group ping-pong schedule as the FP8 kernel. S^T = K Q^T and
 // O^T = V^T P^T both run on v_mfma_f32_32x32x16_bf16, so each lane holds one
-// query (l%32): row maxima and sums are in-lane plus one permlane32 swap, and
-// the probabilities feed the P V instruction straight from registers. V stays
+// query (l%32): row maxima are in-lane plus one permlane32 swap, and the
+// probabilities feed the P V instruction straight from registers. The row
+// sums come from one more (16x16x32) matrix instruction per 16 keys. V stays
 // row-major in LDS (rows permuted); the V^T operand is read with
 // ds_read_b64_tr_b16.
 #include <type_traits>
@@ -55,8 +56,8 @@ __device__ inline int vrow_bf16(int k) { return (k & ~15) | ((k & 3) << 2) | ((k
 // Ping-pong schedule, as in the FP8 kernel: slots separated by workgroup
 // barriers, group 1 (waves 4-7) one phase behind group 0 (waves 0-3), so the
 // two waves of a SIMD alternate between
-//   X_t: O^T += V^T P_{t-1}^T, then S_t^T = K_t Q^T   [matrix cores]
-//   Y_t: mask, maxima, rescale, P_t = 2^((S - m) c) -> BF16, row sum  [vector ALU]
+//   X_t: O^T += V^T P_{t-1}^T and its row sums, then S_t^T = K_t Q^T   [matrix cores]
+//   Y_t: mask, maxima, rescale, P_t = 2^((S - m) c) -> BF16             [vector ALU]
 // Each group copies one operand with direct-to-LDS loads issued at the start
 // of its softmax phase: group 1 loads V_t in slot 2t and waits for it before
 // the barrier closing slot 2t+1; group 0 loads K_{t+1} in slot 2t+1 and waits
@@ -137,7 +138,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   v16f oacc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) oacc[db] = (v16f){};
-  float m = -INFINITY, lsum = 0.0f;
+  float m = -INFINITY;
+  // Row sums of the rounded probabilities on the matrix cores: per 16 keys,
+  // one v_mfma_f32_16x16x32_bf16 of a selector against the P operand. Lane l
+  // of P holds 8 keys of query l%32; in the 16x16 instruction it supplies
+  // column l%16 and the K slots of lane group l/16. The selector (A: row
+  // l%16, K slots of group l/16) is 1 where bit 2 of l equals bit 4, so D
+  // rows 0-3 and 8-11 add lane groups 0 and 2 (query n) and rows 4-7 and
+  // 12-15 groups 1 and 3 (query n + 16); lane l's four D registers (rows
+  // 4 (l/16) ..) then all hold the running sum of query l%32.
+  v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
+  v8bf sel;
+  {
+    const __bf16 e = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.0f : (__bf16)0.0f;
+    sel = (v8bf){e, e, e, e, e, e, e, e};
+  }
   const float c = p.c;
 
   v16f s[L::kNsb];           // S_t^T, from X_t to Y_t
@@ -202,6 +217,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
           fr[jn % kRing] = read_k(jn - kPvSteps);
         oacc[i & 3] = mfma_32x32x16_bf16(fr[i % kRing], pf[i >> 3][(i >> 2) & 1], oacc[i & 3]);
         __builtin_amdgcn_sched_barrier(0);
+        if ((i & 3) == 3) {  // after the fourth use of this P fragment: its row sums
+          rs = mfma_16x16x32_bf16(sel, pf[i >> 3][(i >> 2) & 1], rs);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     } else if (do_qk) {
 #pragma unroll
@@ -238,11 +257,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
       asm volatile("" ::: "memory");
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      lsum *= alpha;
+      rs *= alpha;
     }
-    // P = 2^(S c - m c) rounded to BF16; the row sum adds the rounded pairs
-    // (v_dot2 against (1, 1)), i.e. exactly the weights the P V product uses
-    const v2bf ones2 = {(__bf16)1.0f, (__bf16)1.0f};
+    // P = 2^(S c - m c) rounded to BF16 (the next matrix phase adds the row
+    // sums of exactly these rounded weights)
 #pragma unroll
     for (int sb = 0; sb < L::kNsb; ++sb) {
 #pragma unroll
@@ -253,7 +271,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
           const int r = 8 * hh + 2 * e;
           pw[e] = pack_bf16(__builtin_amdgcn_exp2f(fmaf(s[sb][r], c, nmc)),
                             __builtin_amdgcn_exp2f(fmaf(s[sb][r + 1], c, nmc)));
-          lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pw[e]), ones2, lsum, false);
         }
         pf[sb][hh] = __builtin_bit_cast(v8bf, (v4i){(int)pw[0], (int)pw[1], (int)pw[2], (int)pw[3]});
       }
@@ -289,8 +306,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
     }
   }
 
-  // ---- epilogue: lanes l and l^32 hold partial sums of one query.
-  const float l_tot = sum_xor32(lsum);
+  // ---- epilogue
+  const float l_tot = rs[0];
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
     const float inv = p.dv / l_tot;

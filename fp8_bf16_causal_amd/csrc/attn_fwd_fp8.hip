@@ -411,25 +411,37 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     for (int ks = 0; ks < 2; ++ks) {
       const float bias = ks == 0 ? bias_a : bias_b;
 #pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const v16f& sv = s[2 * ks + (d >> 2)];
-        const int r0 = 4 * (d & 3);
-        uint32_t w = 0;
+      for (int hb = 0; hb < 2; ++hb) {  // block s[2 ks + hb] -> dwords 4 hb .. 4 hb + 3 of P[ks]
+        const v16f& sv = s[2 * ks + hb];
         if constexpr (kExactP) {
-          const float x0 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 0], c, bias));
-          const float x1 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 1], c, bias));
-          const float x2 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 2], c, bias));
-          const float x3 = __builtin_amdgcn_exp2f(fmaf(sv[r0 + 3], c, bias));
-          w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-          w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)w, true);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x0 = __builtin_amdgcn_exp2f(fmaf(sv[4 * j + 0], c, bias));
+            const float x1 = __builtin_amdgcn_exp2f(fmaf(sv[4 * j + 1], c, bias));
+            const float x2 = __builtin_amdgcn_exp2f(fmaf(sv[4 * j + 2], c, bias));
+            const float x3 = __builtin_amdgcn_exp2f(fmaf(sv[4 * j + 3], c, bias));
+            uint32_t w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+            w = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, (int)w, true);
+            P[ks][4 * hb + j] = (int)w;
+          }
         } else {
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 0], c8, bias), 0, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 1], c8, bias), 1, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 2], c8, bias), 2, w);
-          w = __builtin_amdgcn_cvt_pk_u8_f32(fmaf(sv[r0 + 3], c8, bias), 3, w);
+          // the four dwords are built side by side (multiply-adds for byte x,
+          // then the four converts inserting it), so that no instruction
+          // waits on the one just before it
+          uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            float f[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[j] = fmaf(sv[4 * j + x], c8, bias);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_cvt_pk_u8_f32(f[j], x, w[j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) P[ks][4 * hb + j] = (int)w[j];
         }
-        P[ks][d] = (int)w;
-
       }
     }
     sc[0] = 127 - (int)ka;
