@@ -10,6 +10,10 @@ matrix, two matrix products of 2 flop per multiply-add); the figure under the
 literal 2*B*H*S^2*(Dqk+Dv) formula is printed beside it. Peaks are MI355X's
 published dense matrix-core figures: 5.0 PFLOP/s FP8, 2.5 PFLOP/s BF16.
 
+After the timed step, the other full-size workloads (the MLA-shaped and the
+peaked GQA FP8 prefills) and one GPU's share under 8-way head parallelism are
+timed as extra fields, outside the step.
+
 Prints one JSON line. --gpus above 1 is refused: the benchmark runs on one GPU.
 """
 from __future__ import annotations
@@ -27,7 +31,10 @@ sys.path.insert(0, ROOT)
 METRIC = "causal prefill attn TFLOP/s, FP8 & BF16, S=32K hd128; % of MFMA peak"
 PEAK = {"fp8": 5033.2, "bf16": 2516.6}  # TFLOP/s: 256 CU * 4 SIMD * {2048, 1024} flop/clk * 2.4 GHz
 PATHS = ["fp8_mha_s32k", "bf16_mha_s32k"]
-PAGES_TFLOPS = {"fp8_mha_s32k": 2672.0}  # the pages' own FP8 figure on this workload (context)
+# the pages' own FP8 figures on these workloads (context, other builds)
+PAGES_TFLOPS = {"fp8_mha_s32k": 2672.0, "fp8_mla_s32k": 2464.0}
+# the other full-size workloads, timed after the benchmark step (not part of it)
+OTHER_CONFIGS = ["fp8_mla_s32k", "fp8_gqa_s16k_peaked"]
 
 
 # Sources whose text defines each kernel's code and launch: a stored HBM
@@ -188,6 +195,44 @@ def time_tp_shares(full_paths, steps=20, warmup=20):
     return res
 
 
+def time_other_configs(steps=20, warmup=20):
+    """The kernels on the other full-size workloads: the MLA-shaped FP8
+    prefill (head dim 192/128, H=16, S=32K) and the GQA FP8 prefill with
+    peaked scores (Hq=32, Hkv=8, S=16K). Median of `steps` launches, each
+    bracketed by events on the launch stream."""
+    import torch
+
+    import fp8_bf16_causal_amd as fbc
+    from fp8_bf16_causal_amd import synth
+
+    res = {}
+    for name in OTHER_CONFIGS:
+        inp = synth.make_config(name, device="cuda")
+        p = inp.shape
+        out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
+        dq, dk, dv = inp.descale
+        for _ in range(warmup):
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record()
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in ev)[steps // 2]
+        tf = causal_flops(p) / (ms * 1e-3) / 1e12
+        row = {"B": p["B"], "Hq": p["Hq"], "Hkv": p["Hkv"], "S": p["S"], "Dqk": p["Dqk"], "Dv": p["Dv"],
+               "kernel_ms_median": round(ms, 4), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK[inp.dtype], 4)}
+        if name in PAGES_TFLOPS:
+            row["pages_tflops"] = PAGES_TFLOPS[name]
+            row["ratio_to_pages"] = round(tf / PAGES_TFLOPS[name], 3)
+        res[name] = row
+        del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def _power_file():
     """The board's socket-power sensor (hwmon power1_input, microwatts), if the
     driver exposes one."""
@@ -324,6 +369,8 @@ def main():
     ap.add_argument("--energy", action="store_true",
                     help="sustained speed, board power and TFLOP/J on Gaussian vs peaked operands (not a bench line)")
     ap.add_argument("--energy-seconds", type=float, default=4.0, help="untimed and timed seconds per energy case")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the timing of the other full-size workloads (MLA shape, peaked GQA)")
     ap.add_argument("--no-shares", action="store_true",
                     help="skip the timing of one GPU's share under 8-way tensor parallelism")
     ap.add_argument("--fp8-flags", type=int, default=0,
@@ -432,6 +479,8 @@ def main():
             "paths": paths, "roofline": roofline}
     if args.fp8_flags:
         line["fp8_flags"] = args.fp8_flags
+    if not args.no_others and not args.fp8_flags:
+        line["other_configs"] = time_other_configs()
     if not args.no_shares and not args.fp8_flags:
         line["tp8_shares"] = time_tp_shares(paths)
     if not args.no_quant and not args.fp8_flags:
