@@ -144,6 +144,19 @@ def test_fp8_v_ones_gives_exact_ones():
     assert np.all(out == 1.0)
 
 
+@pytest.mark.parametrize("Dqk,structure", [(128, "gaussian"), (128, "peaked"), (192, "gaussian")])
+def test_bf16_v_ones_gives_exact_ones(Dqk, structure):
+    """The BF16 row sums come from a matrix instruction of a 0/1 lane
+    selector against the P operand: with V = 1 they must equal, query by
+    query, the weights the P V product applies, so every output is exactly
+    1.0 (a selector that mixed the lanes of two queries would not)."""
+    inp = synth.make_inputs(B=1, S=1300, Hq=4, Hkv=2, Dqk=Dqk, Dv=128, dtype="bf16", seed=13, structure=structure)
+    inp.v = torch.ones_like(inp.v)
+    _say(f"case bf16 V=1 Dqk={Dqk} {structure}")
+    out = run_gpu(inp).float().cpu().numpy()
+    assert np.all(out == 1.0)
+
+
 def test_fp8_matches_leanp_model_closely():
     """Diagnostic: the kernel follows the FP8-softmax model step by step
     (same tile of 128 keys, same 64-key blocks, same constant, same lazy
