@@ -154,12 +154,6 @@ __device__ inline v4s lds_read_tr16(const uint8_t* p) {
 
 __device__ inline v4i ld_global16(const uint8_t* p) { return *(const v4i*)p; }
 
-// global_load_lds_dwordx4: lane l's 16 bytes from src land at lds_base + 16 l
-// (lds_base is wave-uniform). Completion is tracked by vmcnt.
-__device__ inline void gl_load_lds16(const uint8_t* src, uint8_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(lds_u8*)lds_base, 16,
-                                   0, 0);
-}
 // s_waitcnt vmcnt(0): every vector-memory load of this wave (including
 // direct-to-LDS ones) has completed.
 __device__ inline void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
@@ -178,32 +172,6 @@ __device__ inline void wait_vmem_all_but() {
 // wait_vmem() before the barrier that publishes a direct-to-LDS tile. The
 // memory clobber keeps the compiler from moving memory accesses across it.
 __device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-// Direct-to-LDS copy of one key tile. LDS row r has CS 16-byte chunks, the
-// first CD of which hold bytes [0, 16 CD) of key row k0 + key_of(r) of a
-// global array (base g, row_stride bytes per key row); the remaining chunks of
-// the row (padding) receive a duplicate of its first chunk. Rows past the
-// sequence end read row S - 1 (finite data whose keys every stored query masks).
-// The ROWS * CS chunks are written by 1 KiB instructions spread over NW
-// loading waves; `wave` is the caller's index among them (0 .. NW-1).
-// Offsets are 32-bit: the caller guarantees S * row_stride < 2^32.
-template <int ROWS, int CS, int CD, int NW, typename KeyOf>
-__device__ inline void load_tile_lds(const uint8_t* g, uint32_t row_stride, int k0, int S, uint8_t* lds_tile,
-                                     int wave, int lane, KeyOf key_of) {
-  static_assert(ROWS * CS % 64 == 0, "tile must be a whole number of 1 KiB loads");
-  constexpr int kInsts = ROWS * CS / 64;
-  constexpr int kPerWave = (kInsts + NW - 1) / NW;
-#pragma unroll
-  for (int u = 0; u < kPerWave; ++u) {
-    const int i = wave + NW * u;
-    if (kInsts % NW == 0 || i < kInsts) {
-      const int n = i * 64 + lane, r = n / CS, pos = n - r * CS;
-      const int c = pos < CD ? pos : 0;
-      const int j = min(k0 + key_of(r), S - 1);
-      gl_load_lds16(g + ((uint32_t)j * row_stride + 16u * (uint32_t)c), lds_tile + i * 1024);
-    }
-  }
-}
-
 // Buffer resource (raw, no stride) over `bytes` bytes from `base`. The
 // hardware range-checks every lane of a buffer load against it: lanes at or
 // past the end read zero instead of memory. Word 3 is the gfx9 default
@@ -227,10 +195,12 @@ __device__ inline void buf_load_lds16_at(rsrc_t r, uint32_t voff, uint32_t lds_o
 }
 
 // Direct-to-LDS copy of a key tile through a buffer resource whose range ends
-// at the sequence's last row, so rows past it arrive as zeros. Same LDS row
-// format as load_tile_lds (CS chunks per row, the first CD of them data, the
-// rest a copy of chunk 0). The per-lane source offsets are computed once, so
-// issuing a tile costs no vector instructions. The kInsts 1 KiB instructions
+// at the sequence's last row, so rows past it arrive as zeros. LDS row r has
+// CS 16-byte chunks: the first CD hold bytes [0, 16 CD) of key row key_of(r)
+// (relative to the resource's first row); the lanes writing the padding
+// chunks read from out of range, so they write zeros and fetch nothing. The
+// per-lane source offsets are computed once, so issuing a tile costs no
+// vector instructions. The kInsts 1 KiB instructions
 // are dealt round-robin to the NW waves; the remainder goes to the waves
 // whose (wave + ROT) % NW is below it, so that loaders with different ROT
 // balance each other.
@@ -248,7 +218,7 @@ struct TileLoader {
   template <typename KeyOf>
   __device__ static uint32_t lane_offset(int i, int lane, uint32_t row_stride, KeyOf key_of) {
     const int n = i * 64 + lane, r = n / CS, pos = n - r * CS;
-    return (uint32_t)key_of(r) * row_stride + 16u * (uint32_t)(pos < CD ? pos : 0);
+    return pos < CD ? (uint32_t)key_of(r) * row_stride + 16u * (uint32_t)pos : kOutOfRange;
   }
   template <typename KeyOf>
   __device__ void init(uint32_t row_stride, int wave_, int lane, KeyOf key_of) {

@@ -107,15 +107,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   constexpr int kLoadWaves = kWaves / 2;
   const int lw = wave & (kLoadWaves - 1);  // index within the wave's group
   auto identity = [](int r) { return r; };
+  // per-lane source offsets computed once; each tile goes through a buffer
+  // resource from its first key to the end of key Sk - 1 (rows past it: zeros)
+  TileLoader<BK, 17, 16, kLoadWaves, 0> kld;
+  TileLoader<BK, 9, 8, kLoadWaves, 2> khld;
+  TileLoader<BK, 17, 16, kLoadWaves, 0> vld;
+  // group 1 copies the first K tile, group 0 all later ones
+  kld.init(k_rs, lw, lane, identity);
+  if constexpr (L::kHi) khld.init(k_rs, lw, lane, identity);
+  if (grp == 1) vld.init(v_rs, lw, lane, vrow_bf16);
   auto issue_k = [&](int t) {
     uint8_t* Kl = Kbuf + (t & 1) * L::kKTile;
-    load_tile_lds<BK, 17, 16, kLoadWaves>(Kg, k_rs, t * BK, Sk, Kl, lw, lane, identity);
-    if constexpr (L::kHi)
-      load_tile_lds<BK, 9, 8, kLoadWaves>(Kg + 256, k_rs, t * BK, Sk, Kl + L::kKLoTile, lw, lane, identity);
+    const int k0 = t * BK;
+    const uint32_t bytes = (uint32_t)(Sk - k0) * k_rs;
+    const uint8_t* src = Kg + (size_t)k0 * k_rs;
+    kld.issue(make_rsrc(src, bytes), Kl);
+    if constexpr (L::kHi) khld.issue(make_rsrc(src + 256, bytes - 256), Kl + L::kKLoTile);
   };
   auto issue_v = [&](int t) {
     uint8_t* Vl = Vbuf + (t & 1) * L::kVTile;
-    load_tile_lds<BK, 17, 16, kLoadWaves>(Vg, v_rs, t * BK, Sk, Vl, lw, lane, vrow_bf16);
+    const int k0 = t * BK;
+    vld.issue(make_rsrc(Vg + (size_t)k0 * v_rs, (uint32_t)(Sk - k0) * v_rs), Vl);
   };
 
   // V^T operand of v_mfma_f32_32x32x16_bf16 via ds_read_b64_tr_b16: lane
