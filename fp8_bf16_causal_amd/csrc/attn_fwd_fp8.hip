@@ -101,13 +101,8 @@ struct Fp8Layout {
   static constexpr int kStages = 3;                   // buffers per operand
   static constexpr int kSpare = kStages * (kKTile + kVTile);  // 1 KiB target of idle loads
   static constexpr int kLoop = kSpare + 1024;
-  // head dim 192: Q's first 64 columns (fragment 0) wait in LDS between the
-  // Q K^T phases, 2 KiB per wave (the registers are short at this width)
-  static constexpr bool kQ0Lds = kHi;
-  static constexpr int kQ0 = kLoop;
-  static constexpr int kLoopQ = kLoop + (kQ0Lds ? kWaves * 2048 : 0);
   static constexpr int kEpi = kWaves * kQW * kOStride;
-  static constexpr int kLds = kLoopQ > kEpi ? kLoopQ : kEpi;
+  static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
 };
 
 // V's LDS row for key k of the tile: the low four bits b3 b2 b1 b0 of k
@@ -139,23 +134,22 @@ __device__ inline int vkey_fp8(int r) {
 // instruction stream because the hardware does not track MFMA completion.]
 //
 // Within X_t the operand fragments are read from LDS two MFMA steps ahead in
-// one ring that runs from the P V steps into the Q K steps (K one step ahead
-// at head dim 192); the first two V fragments are read at the end of Y_{t-1},
-// so the matrix cores start at the barrier. Each tile's row sums come from
-// matrix instructions against a ones operand into S's last block, which is
-// free until the fourth Q K step; one register of the result joins the
-// running sum l. At head dim 192 the first Q fragment waits in LDS between
-// tiles. Both keep the registers within budget: a spilled register is
-// reloaded through the vector-memory counter, and that wait would also cover
-// the tile copies still in flight.
+// one ring that runs from the P V steps into the Q K steps; the phase starts
+// by reading the first two V fragments (the softmax phase, the longer of the
+// two, then carries no LDS reads of the next tile). Each tile's row sums come
+// from matrix instructions against a ones operand into S's last block, which
+// is free until the fourth Q K step; one register of the result joins the
+// running sum l. This keeps the registers within budget without spills: a
+// spilled register is reloaded through the vector-memory counter, and that
+// wait would also cover the tile copies still in flight.
 //
 // K/V staging (three buffers per operand): each group copies one operand with
 // direct-to-LDS instructions issued together at the start of its softmax
 // phase (issued later, spread through the phase or in the matrix phase, they
 // measured slower). Group 1 loads V_{t+1} during Y_{t-1} (slot 2t); group 0
 // loads K_{t+2} during Y_t (slot 2t+1). K_t is read in slots 2t and 2t+1, V_t
-// from slot 2t+1 (prefetch at the end of group 0's Y_t) to slot 2t+3: each
-// load overwrites a buffer last read at least one slot before it starts. A
+// in slots 2t+2 and 2t+3 (the P V steps of X_{t+1}): each load overwrites a
+// buffer last read at least one slot before it starts. A
 // wave waits for a tile at the end of the softmax phase of the slot before
 // the tile's first read, with the tile it has just issued still in flight
 // (vmcnt = one tile's loads): about two slots from issue to wait. Every
@@ -206,19 +200,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       qf[t] = (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     }
   }
-  uint8_t* const q0l = lds + L::kQ0 + wave * 2048 + 16 * lane;  // this lane's fragment-0 slot (head dim 192)
-  if constexpr (L::kQ0Lds) {
-    *(v4i*)q0l = (v4i){qf[0][0], qf[0][1], qf[0][2], qf[0][3]};
-    *(v4i*)(q0l + 1024) = (v4i){qf[0][4], qf[0][5], qf[0][6], qf[0][7]};
-  }
-  auto q_frag0 = [&]() {
-    if constexpr (L::kQ0Lds) {
-      const v4i lo = ld_lds16(q0l), hi = ld_lds16(q0l + 1024);
-      return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    } else {
-      return qf[0];
-    }
-  };
 
   // Each tile goes through a buffer resource that starts at its first key and
   // ends with key S - 1: rows past the sequence arrive as zeros (finite
@@ -317,10 +298,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
 
   v16f s[4];     // S_t^T, from X_t to Y_t
   v8i P[2];      // P_t codes (64-key block ks in P[ks]), from Y_t to X_{t+1}
-  v8i vpre[2];   // V_t fragments of PV steps 0 and 1, from the end of Y_t to X_{t+1}
   int sc[2] = {127, 127};  // E8M0 scale bytes of P[0], P[1]: 127 - k
 #pragma unroll
-  for (int q = 0; q < 2; ++q) P[q] = vpre[q] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
+  for (int q = 0; q < 2; ++q) P[q] = (v8i){0, 0, 0, 0, 0, 0, 0, 0};
 
   // X_t: the matrix phase of tile t (P V of tile t-1, then Q K^T of tile t).
   auto phase_x = [&](int tt) {
@@ -338,9 +318,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     // asm definition, no instruction) so it does not occupy registers
     // through the P V half of this phase.
     asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
-    // Q K fragments are read kKA steps ahead (one at head dim 192, where the
-    // registers are short)
-    constexpr int kKA = DQK == 128 ? 2 : 1;
+    // Q K fragments are read kKA steps ahead
+    constexpr int kKA = 2;
     constexpr int kKR = kKA + 1;
     v8i kf[kKR];
     v8i q0;  // Q fragment 0 for the Q K steps
@@ -349,14 +328,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
                         0x38383838, 0x38383838, 0x38383838, 0x38383838};  // e4m3 1.0
       v8i vf[3];
-      vf[0] = vpre[0];
-      vf[1] = vpre[1];
+      vf[0] = read_v(Vl, 0);
+      vf[1] = read_v(Vl, 1);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ks = i >> 2, dvb = i & 3;
         if (i + 2 < 8) vf[(i + 2) % 3] = read_v(Vl, i + 2);
         if (i >= 8 - kKA) kf[i - (8 - kKA)] = read_k(Kl, i - (8 - kKA));  // the first Q K steps
-        if (i == 7) q0 = q_frag0();
+        if (i == 7) q0 = qf[0];
         oacc[dvb] = mfma_32x32x64_fp8(vf[i % 3], P[ks], oacc[dvb], 127, sc[ks]);
         __builtin_amdgcn_sched_barrier(0);
         if (dvb == 3) {
@@ -367,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     } else {
 #pragma unroll
       for (int j = 0; j < kKA; ++j) kf[j] = read_k(Kl, j);
-      q0 = q_frag0();
+      q0 = qf[0];
       s[3] = (v16f){};
     }
     if (do_qk) {
@@ -478,12 +457,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     }
     sc[0] = 127 - (int)ka;
     sc[1] = 127 - (int)kb;
-    // the first two V fragments of X_{tt+1} (V_tt is resident: see above),
-    // read after the codes so that S and the fragments are never live together
-    __builtin_amdgcn_sched_barrier(0);
-    const uint8_t* Vn = Vbuf + ring_offset<L::kStages>(tt, L::kVTile);
-    vpre[0] = read_v(Vn, 0);
-    vpre[1] = read_v(Vn, 1);
   };
 
   if (grp == 0) {
