@@ -482,7 +482,7 @@ def main():
     if not args.no_others and not args.fp8_flags:
         line["other_configs"] = time_other_configs()
     if not args.no_shares and not args.fp8_flags:
-        line["tp8_shares"] = time_tp_shares(paths)
+        line["tp8_shares"] = time_tp_shares({**paths, **line.get("other_configs", {})})
     if not args.no_quant and not args.fp8_flags:
         line["quantize_prologue"] = time_quant_prologue(20, 5)
     if not args.no_cpu_baseline:
