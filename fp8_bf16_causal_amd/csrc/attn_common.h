@@ -14,7 +14,11 @@
 //    cover K in [0, 64), bytes 16-31 cover K in [64, 128); the scale of
 //    (i, 32-wide K block kb) comes from lane i + 16*kb. D lane (j = l%16, g)
 //    register r holds D[4g + r][j].
-//  * global_load_lds_dwordx4: lane l's 16 bytes land at M0 + 16 l.
+//  * v_mfma_f32_16x16x32_bf16: A lane (i = l%16, g = l/16) holds row i at the
+//    K slots of lane group g, B lane (j, g) column j at the same K slots; D
+//    lane (j = l%16, g) register r holds D[4g + r][j].
+//  * buffer_load_dwordx4 ... lds: lane l's 16 bytes land at M0 + 16 l; lanes
+//    whose offset lies past the buffer resource's range write zeros.
 //  * ds_read_b64_tr_b8: within each 16-lane group, lanes 2b and 2b+1 supply
 //    the addresses of the two 8-byte halves of "row" b (b = 0..7); lane c
 //    receives byte c of each of the 8 rows.
