@@ -120,6 +120,24 @@ def test_head_dim_192(dtype, S):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("Dqk", [128, 192])
+def test_batched_gqa_ragged(dtype, Dqk):
+    """Several batch entries, GQA 6/2 and a length that is not a multiple of
+    the 256-row query block or the 128-key tile, at both head dims."""
+    inp = synth.make_inputs(B=3, S=389, Hq=6, Hkv=2, Dqk=Dqk, Dv=128, dtype=dtype, seed=31 + Dqk)
+    full_check(inp, f"{dtype} B3 Hq6 Hkv2 S389 Dqk{Dqk}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("scale", [0.02, 0.3])
+def test_non_default_scale(dtype, scale):
+    """The softmax scale is folded into the base-2 score scale: a small one
+    (nearly flat rows) and a large one (peaked rows, more rescales)."""
+    inp = synth.make_inputs(B=1, S=700, Hq=4, Hkv=2, Dqk=128, Dv=128, dtype=dtype, seed=41, scale=scale)
+    full_check(inp, f"{dtype} scale={scale}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_xcd_grouped_mapping(dtype):
     """B * Hkv divisible by 8 takes the XCD-grouped workgroup order."""
     inp = synth.make_inputs(B=2, S=700, Hq=8, Hkv=4, Dqk=128, Dv=128, dtype=dtype, seed=77)
