@@ -158,8 +158,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   // l%16, K slots of group l/16) is 1 where bit 2 of l equals bit 4, so D
   // rows 0-3 and 8-11 add lane groups 0 and 2 (query n) and rows 4-7 and
   // 12-15 groups 1 and 3 (query n + 16); lane l's four D registers (rows
-  // 4 (l/16) ..) then all hold the running sum of query l%32.
-  v4f rs = {0.0f, 0.0f, 0.0f, 0.0f};
+  // 4 (l/16) ..) then all hold the running sum of query l%32. The eight
+  // instructions of a tile alternate between two accumulators (rs, rs2), so
+  // that issued back to back they do not wait on one another.
+  v4f rs = {0.0f, 0.0f, 0.0f, 0.0f}, rs2 = {0.0f, 0.0f, 0.0f, 0.0f};
   v8bf sel;
   {
     const __bf16 e = ((lane >> 2) & 1) == ((lane >> 4) & 1) ? (__bf16)1.0f : (__bf16)0.0f;
@@ -220,6 +222,15 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
     if (do_pv) {
 #pragma unroll
       for (int j = 0; j < kDepth; ++j) fr[j] = read_v(j);
+      __builtin_amdgcn_sched_barrier(0);
+      // the row sums first: their operands are in registers, so they run
+      // while the first V fragments arrive from LDS
+#pragma unroll
+      for (int j = 0; j < kPvSteps / 4; ++j) {
+        if (j & 1) rs2 = mfma_16x16x32_bf16(sel, pf[j >> 1][j & 1], rs2);
+        else rs = mfma_16x16x32_bf16(sel, pf[j >> 1][j & 1], rs);
+        __builtin_amdgcn_sched_barrier(0);
+      }
 #pragma unroll
       for (int i = 0; i < kPvSteps; ++i) {
         const int jn = i + kDepth;
@@ -229,10 +240,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
           fr[jn % kRing] = read_k(jn - kPvSteps);
         oacc[i & 3] = mfma_32x32x16_bf16(fr[i % kRing], pf[i >> 3][(i >> 2) & 1], oacc[i & 3]);
         __builtin_amdgcn_sched_barrier(0);
-        if ((i & 3) == 3) {  // after the fourth use of this P fragment: its row sums
-          rs = mfma_16x16x32_bf16(sel, pf[i >> 3][(i >> 2) & 1], rs);
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
     } else if (do_qk) {
 #pragma unroll
@@ -270,6 +277,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
       rs *= alpha;
+      rs2 *= alpha;
     }
     // P = 2^(S c - m c) rounded to BF16 (the next matrix phase adds the row
     // sums of exactly these rounded weights)
@@ -319,7 +327,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   }
 
   // ---- epilogue
-  const float l_tot = rs[0];
+  const float l_tot = rs[0] + rs2[0];
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
     const float inv = p.dv / l_tot;

@@ -138,8 +138,9 @@ __device__ inline int vkey_fp8(int r) {
 // by reading the first two V fragments (the softmax phase, the longer of the
 // two, then carries no LDS reads of the next tile). Each tile's row sums come
 // from matrix instructions against a ones operand into S's last block, which
-// is free until the fourth Q K step; one register of the result joins the
-// running sum l. This keeps the registers within budget without spills: a
+// is free until the fourth Q K step; they are issued first, while the V
+// fragments arrive (their operands are in registers), and one register of the
+// result joins the running sum l. This keeps the registers within budget without spills: a
 // spilled register is reloaded through the vector-memory counter, and that
 // wait would also cover the tile copies still in flight.
 //
@@ -330,6 +331,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       v8i vf[3];
       vf[0] = read_v(Vl, 0);
       vf[1] = read_v(Vl, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // the row sums first: their operands are in registers, so they run
+      // while the first V fragments arrive from LDS
+      s[3] = mfma_32x32x64_fp8(ones, P[0], (v16f){}, 127, sc[0]);
+      __builtin_amdgcn_sched_barrier(0);
+      s[3] = mfma_32x32x64_fp8(ones, P[1], s[3], 127, sc[1]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ks = i >> 2, dvb = i & 3;
@@ -338,10 +346,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
         if (i == 7) q0 = qf[0];
         oacc[dvb] = mfma_32x32x64_fp8(vf[i % 3], P[ks], oacc[dvb], 127, sc[ks]);
         __builtin_amdgcn_sched_barrier(0);
-        if (dvb == 3) {
-          s[3] = mfma_32x32x64_fp8(ones, P[ks], ks == 0 ? (v16f){} : s[3], 127, sc[ks]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
       }
     } else {
 #pragma unroll
