@@ -92,16 +92,16 @@ typedef struct {
   pthread_mutex_t lock;
 } job_t;
 
-/* One output row: the definition of causal softmax attention, in fp64; also
- * the row's log-sum-exp ln sum_j exp(s_j) = m + ln l when lse is not NULL.
- * Query i (of Sq) sits at position i + Sk - Sq of the key sequence and sees
- * keys j <= i + Sk - Sq (with Sq = Sk: j <= i). */
-static void one_row(const job_t* J, int h, int i, double* out, double* lse, double* qrow, double* w) {
-  const int Dqk = J->Dqk, Dv = J->Dv;
+/* The softmax weights of row i (of Sq), the definition of causal softmax in
+ * fp64: scores s_j = scale * dq * dk * <q_i, k_j> for the visible keys
+ * j <= last = i + Sk - Sq (with Sq = Sk: j <= i), their max m, and
+ * w[j] = exp(s_j - m). Returns l = sum_j w[j]; *m_out = m. Query i sits at
+ * position i + Sk - Sq of the key sequence. */
+static double row_weights(const job_t* J, int h, int i, double* qrow, double* w, double* m_out) {
+  const int Dqk = J->Dqk;
   const int last = i + (J->Sk - J->Sq); /* the last visible key */
   size_t qoff = (((size_t)J->b * J->Sq + i) * J->Hq + h) * Dqk;
   for (int d = 0; d < Dqk; ++d) qrow[d] = decode_elem(J->q, J->dtype, qoff + d);
-  /* scores s_j = scale * dq * dk * <q_i, k_j> for visible keys j <= last */
   double m = -INFINITY;
   for (int j = 0; j <= last; ++j) {
     const double* kr = J->kd + (size_t)j * Dqk;
@@ -110,12 +110,23 @@ static void one_row(const job_t* J, int h, int i, double* out, double* lse, doub
     w[j] = J->score_scale * acc;
     if (w[j] > m) m = w[j];
   }
-  /* softmax weights relative to the row max, and their sum */
   double l = 0.0;
   for (int j = 0; j <= last; ++j) {
     w[j] = exp(w[j] - m);
     l += w[j];
   }
+  *m_out = m;
+  return l;
+}
+
+/* One output row: the weighted sum of V rows under row_weights' weights,
+ * divided by their sum, times dv; also the row's log-sum-exp
+ * ln sum_j exp(s_j) = m + ln l when lse is not NULL. */
+static void one_row(const job_t* J, int h, int i, double* out, double* lse, double* qrow, double* w) {
+  const int Dv = J->Dv;
+  const int last = i + (J->Sk - J->Sq);
+  double m;
+  const double l = row_weights(J, h, i, qrow, w, &m);
   for (int d = 0; d < Dv; ++d) out[d] = 0.0;
   for (int j = 0; j <= last; ++j) {
     const double* vr = J->vd + (size_t)j * Dv;
@@ -269,31 +280,39 @@ int oracle_attn_f64(const void* q, const void* k, const void* v, int dtype, int 
 
 /*
  * oracle_attn_probs_f64: the full probability matrix P[i][j] of one (b, h)
- * slice, zero above the diagonal. For tiny S only (the "rows of P sum to one"
+ * slice, zero above the diagonal: row i is row_weights' w / l, the weights
+ * one_row applies to V. For tiny S only (the "rows of P sum to one"
  * invariant). Same inputs and readings as oracle_attn_f64.
  */
 int oracle_attn_probs_f64(const void* q, const void* k, int dtype, int B, int Hq, int Hkv, int S, int Dqk,
                           double scale, double dq, double dk, int b, int h, double* P) {
   if (!q || !k || !P || B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Dqk <= 0 || Hq % Hkv) return -1;
+  if (dtype != ORACLE_BF16 && dtype != ORACLE_FP8_E4M3) return -1;
   if (b < 0 || b >= B || h < 0 || h >= Hq) return -1;
   const int g = h / (Hq / Hkv);
-  for (int i = 0; i < S; ++i) {
-    double m = -INFINITY, l = 0.0;
-    double* row = P + (size_t)i * S;
-    for (int j = 0; j < S; ++j) row[j] = 0.0;
-    for (int j = 0; j <= i; ++j) {
-      double acc = 0.0;
-      for (int d = 0; d < Dqk; ++d)
-        acc += decode_elem(q, dtype, (((size_t)b * S + i) * Hq + h) * Dqk + d) *
-               decode_elem(k, dtype, (((size_t)b * S + j) * Hkv + g) * Dqk + d);
-      row[j] = scale * dq * dk * acc;
-      if (row[j] > m) m = row[j];
-    }
-    for (int j = 0; j <= i; ++j) {
-      row[j] = exp(row[j] - m);
-      l += row[j];
-    }
-    for (int j = 0; j <= i; ++j) row[j] /= l;
+  double* kd = (double*)malloc(sizeof(double) * (size_t)S * Dqk);
+  double* qrow = (double*)malloc(sizeof(double) * (size_t)Dqk);
+  double* w = (double*)malloc(sizeof(double) * (size_t)S);
+  int rc = 0;
+  if (!kd || !qrow || !w) {
+    rc = -1;
+    goto done;
   }
-  return 0;
+  for (int j = 0; j < S; ++j) {
+    const size_t ko = (((size_t)b * S + j) * Hkv + g) * Dqk;
+    for (int d = 0; d < Dqk; ++d) kd[(size_t)j * Dqk + d] = decode_elem(k, dtype, ko + d);
+  }
+  job_t J;
+  memset(&J, 0, sizeof J);
+  J.q = q; J.k = k; J.dtype = dtype; J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Sq = S; J.Sk = S;
+  J.Dqk = Dqk; J.score_scale = scale * dq * dk; J.kd = kd; J.b = b; J.g = g;
+  for (int i = 0; i < S; ++i) {
+    double m;
+    const double l = row_weights(&J, h, i, qrow, w, &m);
+    double* row = P + (size_t)i * S;
+    for (int j = 0; j < S; ++j) row[j] = j <= i ? w[j] / l : 0.0;
+  }
+done:
+  free(kd); free(qrow); free(w);
+  return rc;
 }

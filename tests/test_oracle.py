@@ -161,6 +161,53 @@ def test_probability_rows_sum_to_one_and_are_causal(dtype):
     assert np.all(P[~lower] == 0.0) and np.all(P[lower] > 0.0)
 
 
+def _brute_force_probs(qd, kd, b, h, g, scale):
+    """One head's causal softmax matrix, materialised with math.fsum and a
+    log-sum-exp per row (independent of the oracle's code): qd, kd already
+    carry their dequantisation factors; key head g."""
+    S, D = qd.shape[1], qd.shape[3]
+    P = np.zeros((S, S))
+    for i in range(S):
+        s = [scale * math.fsum(qd[b, i, h, d] * kd[b, j, g, d] for d in range(D)) for j in range(i + 1)]
+        top = max(s)
+        lse = top + math.log(math.fsum(math.exp(x - top) for x in s))
+        for j in range(i + 1):
+            P[i, j] = math.exp(s[j] - lse)
+    return P
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_probs_match_brute_force_and_reproduce_the_output(dtype):
+    """oracle.probs on GQA inputs (4 query heads over 2 KV heads, head 3 reads
+    KV head 1), a second batch entry, a softmax scale other than 1/sqrt(D) and
+    per-tensor factors dq, dk far from 1: equal to a brute-force softmax within
+    1e-14, and P @ V * dv equal to oracle.attention's rows within 1e-13. The
+    brute force with the KV head, the scale or a descale changed lands far
+    from it, so a slip of any of them in oracle.probs would fail."""
+    B, S, Hq, Hkv, D = 2, 11, 4, 2, 8
+    inp = synth.make_inputs(B=B, S=S, Hq=Hq, Hkv=Hkv, Dqk=D, Dv=D + 3, dtype=dtype, seed=91, scale=0.83)
+    if dtype == "bf16":
+        dq, dk, dv = 1.0, 1.0, 1.0
+    else:
+        dq, dk, dv = 0.011, 0.0063, 1.7  # dequantised values of order one, factors far from 1
+        inp = synth.AttnInputs(inp.q, inp.k, inp.v, "fp8", inp.scale, (dq, dk, dv))
+    dt = oracle.BF16 if dtype == "bf16" else oracle.FP8_E4M3
+    qd, kd, vd = (t.numpy() for t in _decoded(inp))
+    b, h, g = 1, 3, 1
+    P = oracle.probs(synth.raw_codes(inp.q), synth.raw_codes(inp.k), dt, inp.scale, b, h, dq, dk)
+    ref = _brute_force_probs(qd, kd, b, h, g, inp.scale)
+    assert np.max(np.abs(P - ref)) <= 1e-14
+    # the weights are the ones the oracle's output applies
+    rows = np.array([[b, h, i] for i in range(S)])
+    out = _oracle(inp, rows=rows)
+    assert np.max(np.abs(P @ vd[b, :, g, :] - out)) <= 1e-13
+    # discrimination: each plausible slip moves P by far more than the tolerance
+    for wrong in (_brute_force_probs(qd, kd, b, h, 0, inp.scale),          # KV head h instead of h / (Hq / Hkv)
+                  _brute_force_probs(qd, kd, b, h, g, inp.scale * 1.25),   # another scale
+                  _brute_force_probs(qd, kd / (dk if dtype == "fp8" else 2.0), b, h, g, inp.scale)):  # dk dropped
+        assert np.max(np.abs(P - wrong)) > 1e-3
+
+
 def test_score_shift_invariance():
     """Adding one vector u to every key shifts each row's scores by a constant
     (scale * q_i . u), which softmax ignores. Integer-valued BF16 inputs keep
