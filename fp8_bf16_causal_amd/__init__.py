@@ -33,7 +33,7 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
                     out=None, exact_p=False, block_scale=True, return_lse=False):
     """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
-    factors. Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
+    factors (ValueError for a factor other than 1 with bfloat16). Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
     enqueued on the current stream; with return_lse=True, also a float32
     tensor [B, Hq, S] of each row's log-sum-exp (attn_fwd_lse). k and v may be
     longer than q (Sk > Sq): the queries are then the last Sq positions and
@@ -50,6 +50,9 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
         raise TypeError(f"q must be bfloat16 or float8_e4m3fn, got {q.dtype}")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise TypeError("q, k and v must have the same dtype")
+    if dtype == ATTN_BF16 and any(x is not None and float(x) != 1.0 for x in (descale_q, descale_k, descale_v)):
+        # bfloat16 values are their own: a factor other than 1 would be silently ignored
+        raise ValueError("descale_q/k/v apply to float8_e4m3fn inputs only (bfloat16 inputs take none, or 1.0)")
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [batch, seq, heads, dim]")
     if not (q.is_cuda and k.is_cuda and v.is_cuda and q.device == k.device == v.device):

@@ -3,14 +3,14 @@
 // (layout, ownership, error codes) is documented in include/fp8_bf16_causal.h.
 #include "fp8_bf16_causal.h"
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 
 #include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
 
-#include "attn_common.h"
+#include "attn_params.h"
 #include "attn_launch.h"
 
 namespace {
@@ -60,13 +60,15 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
     if (!finite_positive(dq) || !finite_positive(dk) || !finite_positive(dv)) return ATTN_ERR_INVALID;
   }
   if ((flags & ~(unsigned)(ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE)) != 0u) return ATTN_ERR_INVALID;
-  const int64_t elem = dtype == ATTN_FP8_E4M3 ? 1 : 2;
+  // element counts of the largest tensor, whole and per batch entry, checked
+  // step by step so that no product itself overflows; the kernels address one
+  // batch entry with 32-bit byte offsets (2 bytes per element at most)
   const int64_t dmax = Dqk > Dv ? Dqk : Dv;
-  if ((int64_t)B * Sk * Hq * dmax * 2 > (INT64_C(1) << 62) || (int64_t)B * Sk * Hq * dmax * elem > (INT64_C(1) << 62))
+  int64_t per_batch = 0, whole = 0;
+  if (__builtin_mul_overflow((int64_t)Sk, (int64_t)(Hq > Hkv ? Hq : Hkv), &per_batch) ||
+      __builtin_mul_overflow(per_batch, dmax * 2, &per_batch) || __builtin_mul_overflow(per_batch, (int64_t)B, &whole))
     return ATTN_ERR_INVALID;
-  // the kernels address one batch entry of each tensor with 32-bit offsets
-  const int64_t per_batch_max = (int64_t)Sk * (Hq > Hkv ? Hq : Hkv) * dmax * 2;
-  if (per_batch_max >= (INT64_C(1) << 32)) return ATTN_ERR_INVALID;
+  if (per_batch >= (INT64_C(1) << 32)) return ATTN_ERR_INVALID;
   const int64_t nqb = ((int64_t)S + fbc::kBQ - 1) / fbc::kBQ;
   const int64_t grid = (int64_t)B * Hq * nqb;
   if (grid > 0x7fffffff) return ATTN_ERR_INVALID;

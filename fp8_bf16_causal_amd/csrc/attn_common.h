@@ -1,6 +1,7 @@
 // attn_common.h -- shared pieces of the gfx950 causal prefill attention kernels:
-// vector types, matrix-core and cross-lane wrappers, LDS helpers, the launch
-// parameter block and the workgroup -> (batch, head, query block) mapping.
+// vector types, matrix-core and cross-lane wrappers, LDS helpers and the
+// workgroup -> (batch, head, query block) mapping (the launch parameter block
+// is in attn_params.h).
 //
 // Register layouts used throughout (gfx950, wave64; measured on the device):
 //  * v_mfma_f32_32x32x16_bf16: A lane (i = l%32, g = l/32) holds A[i][8g .. 8g+7],
@@ -35,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "attn_params.h"
+
 namespace fbc {
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -47,30 +50,6 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
-
-// Work decomposition: 8 waves per workgroup (two per SIMD), 32 query rows
-// per wave, 256 query rows per workgroup.
-constexpr int kWaves = 8;
-constexpr int kThreads = kWaves * 64;
-constexpr int kQW = 32;
-constexpr int kBQ = kWaves * kQW;
-constexpr int kXcds = 8;      // MI355X: 8 accelerator complex dies, each with its own L2
-constexpr int kOStride = 272; // epilogue staging: bytes per 128-wide BF16 output row in LDS
-
-struct AttnParams {
-  const void* q;
-  const void* k;
-  const void* v;
-  void* out;
-  int B, Hq, Hkv, S;  // S: query rows
-  int Sk;             // key rows (>= S); query i sits at position i + Sk - S
-  int G;          // Hq / Hkv
-  int nqb;        // query blocks per head, ceil(S / kBQ)
-  int xcd_group;  // 1: every KV head's workgroups run on one XCD
-  float c;        // softmax scale * dq * dk * log2(e) (> 0)
-  float dv;       // output dequantisation factor
-  float* lse;     // NULL, or [B][Hq][S]: each row's log-sum-exp of its logits
-};
 
 constexpr float kLn2 = 0.69314718055994531f;
 

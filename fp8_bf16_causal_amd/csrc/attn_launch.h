@@ -2,7 +2,7 @@
 // the public ABI; see include/fp8_bf16_causal.h for that).
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace fbc {

@@ -118,3 +118,14 @@ def test_prefix_entry_point_argument_checks(Sq, Sk, lse, code):
     a = dict(GOOD)
     assert fbc.attn_fwd_prefix(P, P, P, P, lse, a["B"], a["Hq"], a["Hkv"], Sq, Sk, a["Dqk"], a["Dv"], a["causal"],
                                a["scale"], a["dtype"], None, None, 0) == code
+
+
+def test_flash_attn_func_refuses_descales_with_bf16():
+    """A dequantisation factor other than 1 on bfloat16 inputs would be silently
+    ignored by the kernels: the wrapper refuses it (before any device work)."""
+    import torch
+
+    q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
+    for kw in (dict(descale_q=0.5), dict(descale_k=2.0), dict(descale_v=0.25)):
+        with pytest.raises(ValueError, match="descale"):
+            fbc.flash_attn_func(q, q, q, **kw)
