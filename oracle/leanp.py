@@ -192,3 +192,84 @@ def leanp_attention(qd: np.ndarray, kd: np.ndarray, vd: np.ndarray, scale: float
         else:
             out[n] = dv * o
     return out
+
+
+# ---------------------------------------------------------------- fp32 decisions
+# The code is an integer decided by floating point, so a bit-level comparison
+# with a GPU takes the decision in the GPU's precision: with the score scale c
+# (base 2, per raw score unit), the reference max m and the block exponent k,
+# the pages' 8 x + C with x = c (s - m) + k is formed as one fp32 fused
+# multiply-add of the raw score s with 8c onto a per-(row, block) bias
+# C + 8k - 8c m (itself one fp32 fused multiply-add), then rounded half to
+# even and saturated to [0, 255] by the integer convert.
+
+from fractions import Fraction  # noqa: E402
+
+
+def round_f32(x: Fraction) -> float:
+    """x rounded to the nearest float32 (ties to even), returned as a Python
+    float holding that float32 value. Overflow gives +-inf."""
+    if x == 0:
+        return 0.0
+    sign = -1.0 if x < 0 else 1.0
+    a = abs(x)
+    e = a.numerator.bit_length() - a.denominator.bit_length()  # 2^e <= a < 2^(e+2)
+    if Fraction(2) ** e > a:
+        e -= 1
+    if Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, -126)  # subnormals share the exponent of the smallest normal
+    q = a / Fraction(2) ** (e - 23)  # 24-bit significand scale
+    n, rem = divmod(q.numerator, q.denominator)
+    half = Fraction(rem, q.denominator)
+    if half > Fraction(1, 2) or (half == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    v = math.ldexp(float(n), e - 23)
+    if v > 3.4028234663852886e38:
+        return sign * math.inf
+    return sign * v
+
+
+def fma_f32(a: float, b: float, c: float) -> float:
+    """fp32 fused multiply-add: a*b + c exactly, rounded once to float32
+    (a, b, c are float32 values; infinities follow IEEE rules)."""
+    if not (math.isfinite(a) and math.isfinite(b) and math.isfinite(c)):
+        return float(np.float32(a) * np.float32(b) + np.float32(c))
+    return round_f32(Fraction(a) * Fraction(b) + Fraction(c))
+
+
+def cvt_u8_rne(f: float) -> int:
+    """The integer convert of a code: round half to even, saturate to [0, 255];
+    -inf and NaN give 0."""
+    if math.isnan(f) or f <= 0.0:
+        return 0
+    if f >= 255.0:
+        return 255
+    return int(round(f))  # Python rounds half to even
+
+
+def tile_codes_fp32(s, c: float, C: float = LEANP_C):
+    """Codes of one query row's first 128-key tile, every decision in fp32.
+
+    s: the 128 raw scores of the tile (float32 values; -inf for masked keys),
+    c: the base-2 score scale (a float32 value). On the first tile the
+    reference max m is the tile's max. Each 64-key block b gets
+    k_b = clamp(floor(8 - c (max_b - m)), 0, 127) and the bias
+    C + 8 k_b - 8c m; code_j = convert(8c s_j + bias). Returns
+    (codes [128] int, [k_a, k_b], m)."""
+    f32 = lambda v: float(np.float32(v))  # noqa: E731  one fp32 rounding
+    s = [f32(v) for v in s]
+    c = f32(c)
+    c8 = 8.0 * c
+    blocks = [s[0:BLOCK_KEYS], s[BLOCK_KEYS:2 * BLOCK_KEYS]]
+    mx = [max(b) for b in blocks]
+    m = max(mx)
+    codes, ks = [], []
+    for b, bmax in zip(blocks, mx):
+        t = f32(f32(bmax - m) * c) if math.isfinite(bmax) else -math.inf
+        kf = math.floor(f32(8.0 - t)) if math.isfinite(t) else math.inf
+        k = int(min(max(kf, 0.0), 127.0))
+        bias = fma_f32(-c8, m, f32(f32(C) + 8.0 * k))
+        codes += [cvt_u8_rne(fma_f32(v, c8, bias)) for v in b]
+        ks.append(k)
+    return np.array(codes, dtype=np.int64), ks, m

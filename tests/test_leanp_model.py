@@ -171,3 +171,71 @@ def test_lazy_reference_max_keeps_the_result():
     t = np.linspace(0.0, 8.0, 1001)
     k = leanp.block_exponent(t)
     assert np.all(k >= 0) and np.all(leanp.leanp_code(t + k) <= 120)
+
+
+# ---------------------------------------------------------------- fp32 decisions
+
+def test_round_f32_matches_numpy_single_rounding():
+    """round_f32 of a double equals numpy's float64 -> float32 cast (one
+    correctly rounded step), over normal and subnormal float32 ranges."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-40, 38, 3000),
+                        rng.standard_normal(500) * 1e-42, [0.0, 1.0, -2.5, 3.4e38, 1.17549435e-38]])
+    for v in x:
+        assert leanp.round_f32(Fraction(float(v))) == float(np.float32(v)), v
+
+
+def test_fma_f32_single_rounding():
+    """fma_f32 rounds a*b + c once: where a*b + c is exact in float64 (operands
+    of close magnitude) it equals the float32 cast of that double; ties go to
+    even; and it differs from a two-step (rounded product) evaluation where
+    the product's low bits decide."""
+    from fractions import Fraction
+
+    rng = np.random.default_rng(6)
+    a = rng.standard_normal(2000).astype(np.float32)
+    b = rng.standard_normal(2000).astype(np.float32)
+    c = rng.standard_normal(2000).astype(np.float32)
+    n_exact = 0
+    for x, y, z in zip(a, b, c):
+        d = float(x) * float(y) + float(z)
+        if Fraction(d) == Fraction(float(x)) * Fraction(float(y)) + Fraction(float(z)):
+            n_exact += 1
+            assert leanp.fma_f32(float(x), float(y), float(z)) == float(np.float32(d))
+    assert n_exact > 1500
+    assert leanp.fma_f32(1.0, 1.0, 2.0 ** -24) == 1.0  # tie, even
+    assert leanp.fma_f32(1.0, 1.0, 3 * 2.0 ** -24) == 1.0 + 2.0 ** -22  # tie, even (up)
+    x = 1.0 + 2.0 ** -12
+    # (1 + 2^-12)^2 - 1 = 2^-11 + 2^-24 exactly; a rounded product would lose the 2^-24
+    assert leanp.fma_f32(x, x, -1.0) == 2.0 ** -11 + 2.0 ** -24
+    assert float(np.float32(np.float32(x) * np.float32(x)) - np.float32(1.0)) == 2.0 ** -11
+    assert leanp.fma_f32(-np.inf, 0.5, 3.0) == -np.inf
+
+
+def test_tile_codes_fp32_agree_with_the_model_away_from_ties():
+    """The fp32 code decisions of one tile equal the fp64 model's codes
+    (leanp_code(x + k) with the same reference max and block exponents)
+    wherever 8(x + k) + C is not within 1e-3 of a half-integer; masked keys
+    give code 0 and a fully masked block exponent 127."""
+    rng = np.random.default_rng(8)
+    c = float(np.float32(0.1275))
+    for trial in range(40):
+        s = (rng.standard_normal(128) * rng.uniform(2, 60)).astype(np.float32).astype(np.float64)
+        nvis = int(rng.integers(1, 129))
+        s[nvis:] = -np.inf
+        codes, ks, m = leanp.tile_codes_fp32(s, c)
+        assert codes[nvis:].sum() == 0
+        if nvis <= 64:
+            assert ks[1] == 127
+        for blk in range(2):
+            sl = slice(64 * blk, 64 * blk + 64)
+            vis = np.isfinite(s[sl])
+            if not vis.any():
+                continue
+            x = (s[sl][vis] - m) * c
+            assert ks[blk] == int(leanp.block_exponent(np.max(x)))
+            y = 8.0 * (x + ks[blk]) + leanp.LEANP_C
+            far = np.abs(y - np.floor(y) - 0.5) > 1e-3
+            assert np.array_equal(codes[sl][vis][far], leanp.leanp_code(x + ks[blk])[far])
