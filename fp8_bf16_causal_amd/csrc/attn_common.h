@@ -154,7 +154,13 @@ __device__ inline void wait_vmem_all_but() {
 // flight when another wave overwrites a buffer after the barrier); callers
 // wait_vmem() before the barrier that publishes a direct-to-LDS tile. The
 // memory clobber keeps the compiler from moving memory accesses across it.
-__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// The LDS wait is the compiler's own instruction rather than part of the asm,
+// so the compiler knows that no LDS read is pending after the barrier and
+// inserts no wait of its own before the first LDS reads of the next phase.
+__device__ inline void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+  asm volatile("s_barrier" ::: "memory");
+}
 // Buffer resource (raw, no stride) over `bytes` bytes from `base`. The
 // hardware range-checks every lane of a buffer load against it: lanes at or
 // past the end read zero instead of memory. Word 3 is the gfx9 default

@@ -43,9 +43,11 @@
 //    sum: one more 32x32x64 instruction per 64-key block (a 16x16x128 one
 //    would mix the scales of two queries in one K block).
 //  * K and V are copied global -> LDS by direct-to-LDS loads (no staging
-//    registers) into padded row-major tiles (at head dim 192, K's first 128
-//    columns chunk-major without padding); V's rows are permuted so that the
-//    transposing reads building the V^T operand are free of bank conflicts.
+//    registers) into row-major tiles of 128-byte rows whose 16-byte chunks
+//    are XOR-swizzled per row, so that the reads of the Q K and P V steps
+//    (including the transposing reads building the V^T operand) are free of
+//    bank conflicts without padding (at head dim 192, K's first 128 columns
+//    chunk-major, its last 64 in padded rows).
 #include <type_traits>
 
 #include "attn_common.h"
@@ -83,42 +85,60 @@ struct KLoLoader {
   }
 };
 
+// Tiles of 128-byte rows without padding (K at head dim 128, V at both head
+// dims): the 16-byte chunk c of row r sits at byte r * 128 + 16 (c ^ swz(r)).
+// A 1 KiB direct-to-LDS instruction then fills 8 whole rows, each lane
+// fetching one chunk (8 lanes cover a row's 128 contiguous bytes), and a
+// tile is exactly 16 instructions, four per wave of the loading group.
+// kswz makes the ds_read_b128 of the Q K steps (lanes 0-31 read rows 0-31 at
+// one chunk) free of bank conflicts: any 8 consecutive rows, and the 8 even
+// or 8 odd rows of any 16, get distinct chunk positions. vswz does the same
+// for the ds_read_b64_tr_b8 of the P V steps, where a 16-lane group reads one
+// chunk of the 8 rows {0-3, 8-11} (or {4-7, 12-15}) of a 16-key group and
+// two groups read neighbouring chunks of the same rows.
+__device__ inline int kswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ inline int vswz(int r) { return (r & 3) | ((r >> 1) & 4); }
+
+template <int NW, int (*Swz)(int)>
+struct SwizLoader {
+  static constexpr int kRegs = 16 / NW;  // 1 KiB instructions per wave
+  static_assert(16 % NW == 0, "a tile is 16 instructions");
+  uint32_t off[kRegs];
+  int wave;
+  template <typename KeyOf>
+  __device__ void init(uint32_t row_stride, int wave_, int lane, KeyOf) {
+    wave = wave_;
+#pragma unroll
+    for (int u = 0; u < kRegs; ++u) {
+      const int r = 8 * (wave + NW * u) + (lane >> 3), c = (lane & 7) ^ Swz(r);
+      off[u] = (uint32_t)r * row_stride + 16u * (uint32_t)c;
+    }
+  }
+  __device__ void issue_spare(rsrc_t r, uint32_t lds_tile, uint32_t, int u) const {
+    buf_load_lds16_at(r, off[u], lds_tile + (uint32_t)(wave + NW * u) * 1024u);
+  }
+};
+
 template <int DQK>
 struct Fp8Layout {
   static constexpr int kBK = 128;                     // keys per tile
   static constexpr int kDv = 128;
   static constexpr bool kHi = DQK == 192;             // K columns 128..191 kept apart
-  // LDS rows carry one 16-byte padding chunk, so that a row's chunks sit at
-  // additive offsets and consecutive rows start in different bank groups.
-  static constexpr int kKLoStride = 144;              // K[:, 0:128]
-  static constexpr int kKHiStride = 80;               // K[:, 128:192]
-  static constexpr int kVStride = 144;                // V
-  static constexpr bool kKCm = kHi;                   // K[:, 0:128] chunk-major, unpadded (KLoLoader)
-  static constexpr int kKLoTile = kKCm ? kBK * 128 : kBK * kKLoStride;
+  // K[:, 128:192] rows carry one 16-byte padding chunk, so that a row's
+  // chunks sit at additive offsets and consecutive rows start in different
+  // bank groups.
+  static constexpr int kKHiStride = 80;
+  static constexpr bool kKCm = kHi;                   // K[:, 0:128] chunk-major (KLoLoader), else swizzled
+  static constexpr int kKLoTile = kBK * 128;
   static constexpr int kKHiTile = kHi ? kBK * kKHiStride : 0;
   static constexpr int kKTile = kKLoTile + kKHiTile;
-  static constexpr int kVTile = kBK * kVStride;
+  static constexpr int kVTile = kBK * 128;            // swizzled
   static constexpr int kStages = 3;                   // buffers per operand
   static constexpr int kSpare = kStages * (kKTile + kVTile);  // 1 KiB target of idle loads
   static constexpr int kLoop = kSpare + 1024;
   static constexpr int kEpi = kWaves * kQW * kOStride;
   static constexpr int kLds = kLoop > kEpi ? kLoop : kEpi;
 };
-
-// V's LDS row for key k of the tile: the low four bits b3 b2 b1 b0 of k
-// become b3 b1 b0 b2. One ds_read_b64_tr_b8 pass (32 lanes) reads the eight
-// keys {0-3, 8-11} or {4-7, 12-15} of a 16-key group, 32 bytes each; they
-// land on the eight even or the eight odd rows of the group, whose 144-byte
-// strides put them in eight distinct groups of 8 banks.
-__device__ inline int vrow_fp8(int k) {
-  const int x = k & 15;
-  return (k & ~15) | ((x >> 3) & 1) << 3 | (x & 3) << 1 | ((x >> 2) & 1);
-}
-// the key held by V's LDS row r (inverse of vrow_fp8)
-__device__ inline int vkey_fp8(int r) {
-  const int n = r & 15;
-  return (r & ~15) | ((n >> 3) & 1) << 3 | (n & 1) << 2 | (n >> 1) & 3;
-}
 
 // Ping-pong schedule. The workgroup's 8 waves form two groups (waves w and
 // w + 4 share a SIMD). Time is cut into slots separated by workgroup
@@ -133,8 +153,9 @@ __device__ inline int vkey_fp8(int r) {
 // cores while the other computes probabilities, order enforced by the
 // instruction stream because the hardware does not track MFMA completion.]
 //
-// Within X_t the operand fragments are read from LDS two MFMA steps ahead in
-// one ring that runs from the P V steps into the Q K steps; the phase starts
+// Within X_t the operand fragments are read from LDS two MFMA steps ahead (K
+// three at head dim 128) in one ring that runs from the P V steps into the
+// Q K steps; the phase starts
 // by reading the first two V fragments (the softmax phase, the longer of the
 // two, then carries no LDS reads of the next tile). Each tile's row sums come
 // from matrix instructions against a ones operand into S's last block, which
@@ -208,9 +229,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // tiles, group 1 (waves 4-7) V tiles.
   constexpr int kGroupWaves = kWaves / 2;
   const int gw = wave & (kGroupWaves - 1);
-  std::conditional_t<L::kKCm, KLoLoader, TileLoader<L::kBK, 9, 8, kGroupWaves, 0>> kld;
+  std::conditional_t<L::kKCm, KLoLoader, SwizLoader<kGroupWaves, kswz>> kld;
   TileLoader<L::kBK, 5, 4, kGroupWaves, 2> khld;
-  TileLoader<L::kBK, 9, 8, kGroupWaves, 0> vld;
+  SwizLoader<kGroupWaves, vswz> vld;
   constexpr int kKLoads = decltype(kld)::kRegs + (L::kHi ? decltype(khld)::kRegs : 0);
   constexpr int kVLoads = decltype(vld)::kRegs;
   // load u of this wave's share of K tile t (u = 0 .. kKLoads-1)
@@ -249,35 +270,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // (the key the S^T accumulator of lane (., g) holds in register 4 e + x).
   // Read j (bytes 8j .. 8j+7) covers keys 16 j + 64 ks + {8 e' + 4 g + x}: in
   // each 16-lane group, lanes 2k and 2k+1 address the two 8-byte halves of
-  // the 16 dv columns of the k-th of those keys. d-block dvb adds 32 dvb.
-  int vrd;
+  // the 16 dv columns of the k-th of those keys. d-block dvb reads dv columns
+  // 32 dvb + 16 (G & 1) .. +15, logical chunk 2 dvb + (G & 1) of the key's row;
+  // vrd[dvb] is that chunk's swizzled offset in the lane's row (the swizzle
+  // depends on key bits 0, 1 and 3 only, the same for every j and ks).
+  int vrd[4];
   {
     const int G = lane >> 4, cc = lane & 15, k = cc >> 1;
     const int key = 8 * (k >> 2) + 4 * (G >> 1) + (k & 3);
-    vrd = vrow_fp8(key) * L::kVStride + 16 * (G & 1) + 8 * (cc & 1);
+    const int h = (G & 1) ^ vswz(key);
+#pragma unroll
+    for (int dvb = 0; dvb < 4; ++dvb) vrd[dvb] = key * 128 + 16 * ((2 * dvb) ^ h) + 8 * (cc & 1);
   }
-  // K operand: block sb reads row sb*32 + l32, chunks 4 t6 + g and 4 t6 + 2 + g
-  const int krd = L::kKCm ? (l32 >> 4) * 2048 + g * 256 + (l32 & 15) * 16 : l32 * L::kKLoStride + 16 * g;
+  // K operand: block sb reads row sb*32 + l32, logical chunks 4 t6 + g and
+  // 4 t6 + 2 + g; krd[q] is the swizzled offset of chunk g + 2q in the lane's
+  // row (head dim 128). At head dim 192 the chunk-major part is additive.
+  int krd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    krd[q] = L::kKCm ? (l32 >> 4) * 2048 + g * 256 + (l32 & 15) * 16 + 512 * q : l32 * 128 + 16 * ((g + 2 * q) ^ kswz(l32));
   const int khrd = l32 * L::kKHiStride + 16 * g;
 
   // PV step i = 4 ks + dvb
   auto read_v = [&](const uint8_t* Vl, int i) {
-    const uint8_t* vp = Vl + vrd + 64 * (i >> 2) * L::kVStride + 32 * (i & 3);
+    const uint8_t* vp = Vl + vrd[i & 3] + 64 * 128 * (i >> 2);
     const v2i r0 = lds_read_tr8(vp);
-    const v2i r1 = lds_read_tr8(vp + 16 * L::kVStride);
-    const v2i r2 = lds_read_tr8(vp + 32 * L::kVStride);
-    const v2i r3 = lds_read_tr8(vp + 48 * L::kVStride);
+    const v2i r1 = lds_read_tr8(vp + 16 * 128);
+    const v2i r2 = lds_read_tr8(vp + 32 * 128);
+    const v2i r3 = lds_read_tr8(vp + 48 * 128);
     return (v8i){r0.x, r0.y, r1.x, r1.y, r2.x, r2.y, r3.x, r3.y};
   };
   // QK step i = t6 * 4 + sb: K rows sb*32 + l32, bytes 64 t6 + 16 g and +32
   auto read_k = [&](const uint8_t* Kl, int i) {
     const int sb = i & 3, t6 = i >> 2;
-    // the second read is chunk + 2: 512 bytes on in the chunk-major part, 32 in a row-major one
-    const bool cm = L::kKCm && t6 < 2;
-    const uint8_t* kp = t6 >= 2 ? Kl + L::kKLoTile + sb * 32 * L::kKHiStride + khrd
-                        : L::kKCm ? Kl + sb * 4096 + krd + 1024 * t6
-                                  : Kl + sb * 32 * L::kKLoStride + krd + 64 * t6;
-    const v4i lo = ld_lds16(kp), hi = ld_lds16(kp + (cm ? 512 : 32));
+    if (t6 >= 2) {
+      const uint8_t* kp = Kl + L::kKLoTile + sb * 32 * L::kKHiStride + khrd;
+      const v4i lo = ld_lds16(kp), hi = ld_lds16(kp + 32);
+      return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+    const uint8_t* kp = Kl + sb * 4096;
+    const v4i lo = ld_lds16(kp + krd[2 * t6]), hi = ld_lds16(kp + krd[2 * t6 + 1]);
     return (v8i){lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
   };
 
@@ -306,8 +338,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // X_t: the matrix phase of tile t (P V of tile t-1, then Q K^T of tile t).
   auto phase_x = [&](int tt) {
     // ================= X_tt: matrix phase
-    // One operand ring, two MFMA steps deep, runs through the P V steps into
-    // the Q K steps; scheduling barriers keep the compiler from hoisting
+    // One operand ring (V two MFMA steps deep, K kKA) runs through the P V
+    // steps into the Q K steps; scheduling barriers keep the compiler from hoisting
     // every LDS read of the phase to its top.
     __builtin_amdgcn_s_setprio(1);
     const bool do_pv = tt >= 1 && tt - 1 < wave_tiles;
@@ -319,8 +351,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     // asm definition, no instruction) so it does not occupy registers
     // through the P V half of this phase.
     asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
-    // Q K fragments are read kKA steps ahead
-    constexpr int kKA = 2;
+    // Q K fragments are read kKA steps ahead (three at head dim 128; two at
+    // 192, where the registers for a third are not free)
+    constexpr int kKA = DQK == 128 ? 3 : 2;
     constexpr int kKR = kKA + 1;
     v8i kf[kKR];
     v8i q0;  // Q fragment 0 for the Q K steps
@@ -473,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
       k_tile(1)(u);
     }
   } else {
-    vld.init(v_rs, gw, lane, vkey_fp8);
+    vld.init(v_rs, gw, lane, 0);
 #pragma unroll
     for (int u = 0; u < kVLoads; ++u) {
       v_tile(0)(u);
