@@ -10,9 +10,15 @@ matrix, two matrix products of 2 flop per multiply-add); the figure under the
 literal 2*B*H*S^2*(Dqk+Dv) formula is printed beside it. Peaks are MI355X's
 published dense matrix-core figures: 5.0 PFLOP/s FP8, 2.5 PFLOP/s BF16.
 
-After the timed step, the other full-size workloads (the MLA-shaped and the
-peaked GQA FP8 prefills) and one GPU's share under 8-way head parallelism are
-timed as extra fields, outside the step.
+Before the warmup steps, steps run back to back for a few seconds untimed
+(--settle-seconds) so that the timed ones run at the sustained, power-limited
+clock rather than the idle boost. The GPU clock is sampled (driver metrics
+through amdsmi, or sysfs) while the timed steps run and reported beside them, with the mean kernel time of the
+first and the last quarter of the timed launches. After the timed steps each
+path also runs alone under a sustained load (4 s untimed, then about 2 s
+timed, clock sampled), and the other full-size workloads (the MLA-shaped and
+the peaked GQA FP8 prefills) and one GPU's share under 8-way head parallelism
+are timed as extra fields, outside the step.
 
 Prints one JSON line. --gpus above 1 is refused: the benchmark runs on one GPU.
 """
@@ -242,6 +248,130 @@ def _power_file():
     return files[0] if files else None
 
 
+class ClockSampler:
+    """Samples the GPU's current graphics clock from a reader thread while
+    kernels run (every `period` s): the mean over the 8 XCDs' current gfxclk
+    from the driver's metrics table through amdsmi, else amdsmi's single GFX
+    clock, else the current line of sysfs pp_dpm_sclk. File and library reads
+    only; nothing is sent to the GPU's queues."""
+
+    def __init__(self, period=0.01):
+        import threading
+
+        self.period, self.samples, self.source = period, [], None
+        self._stop = threading.Event()
+        self._thread = None
+        self._read = self._pick_source()
+
+    def _pick_source(self):
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            h = amdsmi.amdsmi_get_processor_handles()[0]
+
+            def metrics():
+                v = amdsmi.amdsmi_get_gpu_metrics_info(h).get("current_gfxclk")
+                v = [x for x in (v if isinstance(v, list) else [v]) if isinstance(x, (int, float)) and 0 < x < 10000]
+                return sum(v) / len(v) if v else None
+
+            if metrics() is not None:
+                self.source = "amdsmi gpu_metrics current_gfxclk (mean over XCDs)"
+                return metrics
+
+            def clock():
+                return float(amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"])
+
+            clock()
+            self.source = "amdsmi clock_info GFX"
+            return clock
+        except Exception:
+            pass
+        import glob
+        import re
+
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        if files:
+            def sysfs():
+                with open(files[0]) as f:
+                    for ln in f:
+                        if ln.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*Mhz", ln, re.I)
+                            return float(m.group(1)) if m else None
+                return None
+
+            self.source = files[0]
+            return sysfs
+        return None
+
+    def _loop(self):
+        while not self._stop.is_set():
+            try:
+                v = self._read()
+            except Exception:
+                v = None
+            if v:
+                self.samples.append(v)
+            time.sleep(self.period)
+
+    def __enter__(self):
+        import threading
+
+        if self._read:
+            self._thread = threading.Thread(target=self._loop, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread:
+            self._thread.join()
+
+    def mean_mhz(self):
+        return round(sum(self.samples) / len(self.samples), 1) if self.samples else None
+
+
+def sustained(inputs, launch, seconds_warm, seconds_timed):
+    """Each path alone, back to back: `seconds_warm` of untimed launches so the
+    clock settles under the power limit, then about `seconds_timed` of timed
+    launches (events on the launch stream around the whole loop) with the
+    clock sampled meanwhile."""
+    import torch
+
+    res = {}
+    for n in inputs:
+        p = inputs[n].shape
+        kind = inputs[n].dtype
+        launch(n)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        k = 0
+        while time.perf_counter() - t0 < seconds_warm:
+            for _ in range(10):
+                launch(n)
+            torch.cuda.synchronize()
+            k += 10
+        per = (time.perf_counter() - t0) / k
+        reps = max(10, int(seconds_timed / per))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with ClockSampler() as ck:
+            e0.record()
+            for _ in range(reps):
+                launch(n)
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = causal_flops(p) / (ms * 1e-3) / 1e12
+        mhz = ck.mean_mhz()
+        res[n] = {"warm_s": seconds_warm, "launches_timed": reps, "kernel_ms_mean": round(ms, 4),
+                  "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK[kind], 4), "sclk_mhz": mhz,
+                  "clock_samples": len(ck.samples),
+                  "frac_of_peak_at_clock": None if not mhz else round(tf / (PEAK[kind] * mhz / 2400.0), 4)}
+        if n in PAGES_TFLOPS:
+            res[n]["ratio_to_pages"] = round(tf / PAGES_TFLOPS[n], 3)
+    return res
+
+
 def energy_study(seconds):
     """Sustained throughput, board power and energy efficiency of the FP8 and
     BF16 kernels on Gaussian and peaked operands of the same 32K shape (the
@@ -358,7 +488,10 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=400, help="untimed steps first (the default, about 5 s, lets the clock settle)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the timed ones")
+    ap.add_argument("--settle-seconds", type=float, default=4.0,
+                    help="back-to-back untimed steps for this long before the warmup steps, so that the timed steps "
+                         "run at the sustained (power-limited) clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=65536, help="rows per path in the CPU-baseline sample (about 15 s of oracle time on 16 cores)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -373,6 +506,9 @@ def main():
                     help="skip the timing of the other full-size workloads (MLA shape, peaked GQA)")
     ap.add_argument("--no-shares", action="store_true",
                     help="skip the timing of one GPU's share under 8-way tensor parallelism")
+    ap.add_argument("--no-sustained", action="store_true",
+                    help="skip the sustained-clock timing of each path (4 s warm, 2 s timed, clock sampled)")
+    ap.add_argument("--sustained-seconds", type=float, default=4.0, help="warm seconds per path in the sustained timing")
     ap.add_argument("--fp8-flags", type=int, default=0,
                     help="ATTN_FLAG_* bits for the FP8 launches (1 exact P, 2 no block scaling): ablations only")
     args = ap.parse_args()
@@ -412,6 +548,13 @@ def main():
         ab = dict(exact_p=bool(args.fp8_flags & 1), block_scale=not (args.fp8_flags & 2)) if i.dtype == "fp8" else {}
         fbc.flash_attn_func(i.q, i.k, i.v, i.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n], **ab)
 
+    # settle the clock: the kernels drive the board to its power limit within
+    # seconds, and the clock drops from its idle boost to the sustained one
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_seconds:
+        for n in names:
+            launch(n)
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         for n in names:
             launch(n)
@@ -422,14 +565,16 @@ def main():
           for n in names}
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record()
-    for s in range(args.steps):
-        for n in names:
-            ev[n][s][0].record()
-            launch(n)
-            ev[n][s][1].record()
-    stop.record()
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        start.record()
+        for s in range(args.steps):
+            for n in names:
+                ev[n][s][0].record()
+                launch(n)
+                ev[n][s][1].record()
+        stop.record()
+        torch.cuda.synchronize()
+    sclk_run = clock.mean_mhz()
     total_ms = start.elapsed_time(stop)
     ms_per_step = total_ms / args.steps
 
@@ -447,12 +592,15 @@ def main():
         paths[n] = {"kernel_ms_avg": round(avg, 4), "kernel_ms_median": round(med, 4), "kernel_ms_min": round(min(ms), 4),
                     "tflops": round(tf, 1), "tflops_literal_2x": round(2 * tf, 1),
                     "peak_tflops": PEAK[kind], "frac_of_peak": round(tf / PEAK[kind], 4)}
+        q = max(1, len(ms) // 4)
+        paths[n]["kernel_ms_first_quarter"] = round(sum(ms[:q]) / q, 4)
+        paths[n]["kernel_ms_last_quarter"] = round(sum(ms[-q:]) / q, 4)
+        if sclk_run:  # the clock sampled during these timed steps (both paths alternate)
+            paths[n]["frac_of_peak_at_run_clock"] = round(tf / (PEAK[kind] * sclk_run / 2400.0), 4)
         ck = profiled_line(CLOCK_FILE, n, kind)
-        if ck:  # sustained clock of the same kernel in the committed rocprofv3 profile
-            mhz = float(ck["sclk_mhz"])
-            paths[n]["sclk_mhz_profiled"] = mhz
-            paths[n]["frac_of_peak_at_profiled_clock"] = round(tf / (PEAK[kind] * mhz / 2400.0), 4)
-            paths[n]["mfma_busy_profiled"] = float(ck["mfma_busy"])
+        if ck:  # figures of the same kernel in the committed rocprofv3 counter run (another run)
+            paths[n]["profile_sclk_mhz"] = float(ck["sclk_mhz"])
+            paths[n]["profile_mfma_busy"] = float(ck["mfma_busy"])
         if n in PAGES_TFLOPS:
             paths[n]["pages_tflops"] = PAGES_TFLOPS[n]
             paths[n]["ratio_to_pages"] = round(tf / PAGES_TFLOPS[n], 3)
@@ -476,9 +624,13 @@ def main():
             "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "+".join(sorted({inputs[n].dtype for n in names})), "data": "synthetic",
             "config": cfg, "frac_of_peak": round(ideal_s / (ms_per_step * 1e-3), 4),
+            "clock_settle_s": args.settle_seconds, "sclk_mhz_run": sclk_run, "sclk_source": clock.source,
+            "sclk_samples_run": len(clock.samples),
             "paths": paths, "roofline": roofline}
     if args.fp8_flags:
         line["fp8_flags"] = args.fp8_flags
+    if not args.no_sustained:
+        line["sustained"] = sustained(inputs, launch, args.sustained_seconds, 2.0)
     if not args.no_others and not args.fp8_flags:
         line["other_configs"] = time_other_configs()
     if not args.no_shares and not args.fp8_flags:

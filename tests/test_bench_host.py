@@ -54,3 +54,21 @@ def test_balance_bound_of_causal_grids():
         b = bench.balance_bound(B, Hq, Hkv, S)
         assert 0 < b <= 1
     assert bench.balance_bound(1, 4, 4, 32768) > 0.98
+
+
+def test_clock_sampler_averages_its_samples():
+    """The clock sampler's thread reads a source until stopped; with no source
+    (no driver here) it reports nothing instead of a guess."""
+    import time
+
+    ck = bench.ClockSampler(period=0.001)
+    vals = iter([1700.0, 1900.0] * 1000)
+    ck._read = lambda: next(vals)
+    with ck:
+        time.sleep(0.05)
+    assert ck.samples and abs(ck.mean_mhz() - 1800.0) <= 100.0
+    empty = bench.ClockSampler()
+    empty._read = None
+    with empty:
+        pass
+    assert empty.mean_mhz() is None and empty.samples == []
