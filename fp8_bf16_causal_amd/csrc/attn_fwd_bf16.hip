@@ -53,16 +53,16 @@ struct Bf16Layout {
 // swap puts those 4 rows 4 bank groups apart under the 272-byte stride.
 __device__ inline int vrow_bf16(int k) { return (k & ~15) | ((k & 3) << 2) | ((k >> 2) & 3); }
 
-// Ping-pong schedule, as in the FP8 kernel: slots separated by workgroup
-// barriers, group 1 (waves 4-7) one phase behind group 0 (waves 0-3), so the
-// two waves of a SIMD alternate between
+// Ping-pong schedule, as in the FP8 kernel: group 1 (waves 4-7) one phase
+// behind group 0 (waves 0-3), one workgroup barrier per tile, so the two
+// waves of a SIMD alternate between
 //   X_t: O^T += V^T P_{t-1}^T and its row sums, then S_t^T = K_t Q^T   [matrix cores]
 //   Y_t: mask, maxima, rescale, P_t = 2^((S - m) c) -> BF16             [vector ALU]
 // Each group copies one operand with direct-to-LDS loads issued at the start
-// of its softmax phase: group 1 loads V_t in slot 2t and waits for it before
-// the barrier closing slot 2t+1; group 0 loads K_{t+1} in slot 2t+1 and waits
-// before the barrier closing that slot (K_{t+1} is first read in slot 2t+2).
-// Each load overwrites a buffer last read at least one slot earlier, so double
+// of its softmax phase: group 1 loads V_t before X_t and waits for it after
+// X_t; group 0 loads K_{t+1} after X_t and waits at the end of Y_t; both
+// waits precede the barrier after which the tile is first read. Each load
+// overwrites a buffer last read before the previous barrier, so double
 // buffers suffice; splitting the loads (and their address arithmetic) between
 // the groups keeps their softmax phases the same length.
 template <int DQK, int BK>
@@ -301,28 +301,27 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   wait_vmem();
   lds_barrier();
 
-  // One copy of the slot loop per group (2 slots per iteration): same
-  // barriers in the same slots, simpler live ranges. Group 0 stages K tiles,
-  // group 1 V tiles.
+  // One copy of the tile loop per group (simpler live ranges), one barrier
+  // B_t per tile. Group 0 stages K tiles, group 1 V tiles; between B_{t-1}
+  // and B_t, K_{t+1} and V_t overwrite the buffers of K_{t-1} and V_{t-2},
+  // last read by X_{t-1} before B_{t-1}, while X_t reads K_t and V_{t-1}.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
-      phase_x(t);                              // slot 2t: X_t
-      lds_barrier();
-      if (t < n_tiles) {                       // slot 2t + 1: Y_t, loads K_{t+1}
+      phase_x(t);                              // X_t
+      if (t < n_tiles) {                       // Y_t, loads K_{t+1}
         if (t + 1 < n_tiles) issue_k(t + 1);
         if (t < wave_tiles) phase_y(t);
-        wait_vmem();                           // K_{t+1} is first read in slot 2t + 2
+        wait_vmem();                           // K_{t+1} is first read in X_{t+1}
       }
-      lds_barrier();
+      lds_barrier();                           // B_t
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      if (t < n_tiles) issue_v(t);            // slot 2t: Y_{t-1}, loads V_t
+      if (t < n_tiles) issue_v(t);            // Y_{t-1}, loads V_t
       if (t >= 1 && t - 1 < wave_tiles) phase_y(t - 1);
-      lds_barrier();
-      phase_x(t);                              // slot 2t + 1: X_t
-      if (t < n_tiles) wait_vmem();            // slot 2t's loads are first read in slot 2t + 2
-      lds_barrier();
+      phase_x(t);                              // X_t
+      if (t < n_tiles) wait_vmem();            // V_t is first read in X_{t+1}
+      lds_barrier();                           // B_t
     }
   }
 

@@ -141,13 +141,16 @@ struct Fp8Layout {
 };
 
 // Ping-pong schedule. The workgroup's 8 waves form two groups (waves w and
-// w + 4 share a SIMD). Time is cut into slots separated by workgroup
-// barriers; in slot p group 0 runs its phase p and group 1 its phase p - 1.
-// A wave's phases alternate
+// w + 4 share a SIMD). Group 0 runs X_t then Y_t, group 1 Y_{t-1} then X_t,
+// where a wave's phases alternate
 //   X_t: O^T += V^T P_{t-1}^T (and the row-sum MFMAs), then S_t^T = K_t Q^T  [matrix cores]
 //   Y_t: softmax of S_t: maxima, block exponents, Lean P codes, rescale       [vector ALU]
 // so on every SIMD one wave issues matrix instructions while its partner
-// computes probabilities, and they swap at the next barrier.
+// computes probabilities, then they swap. One workgroup barrier per tile,
+// after group 0's Y_t and group 1's X_t, orders the tile copies (below); the
+// swap in the middle of a tile is left to the instruction stream (a wave that
+// finishes its phase early starts the next one, and the matrix wave keeps the
+// higher issue priority).
 // [spbcomputers.ru ZYFA article and captivela.com "Zyphra Luncurkan ZYFA",
 // sections on the three techniques: two waves per SIMD, one on the matrix
 // cores while the other computes probabilities, order enforced by the
@@ -168,16 +171,15 @@ struct Fp8Layout {
 // K/V staging (three buffers per operand): each group copies one operand with
 // direct-to-LDS instructions issued together at the start of its softmax
 // phase (issued later, spread through the phase or in the matrix phase, they
-// measured slower). Group 1 loads V_{t+1} during Y_{t-1} (slot 2t); group 0
-// loads K_{t+2} during Y_t (slot 2t+1). K_t is read in slots 2t and 2t+1, V_t
-// in slots 2t+2 and 2t+3 (the P V steps of X_{t+1}): each load overwrites a
-// buffer last read at least one slot before it starts. A
-// wave waits for a tile at the end of the softmax phase of the slot before
-// the tile's first read, with the tile it has just issued still in flight
-// (vmcnt = one tile's loads): about two slots from issue to wait. Every
-// softmax phase issues the same loads, also for tiles past the workgroup's
-// last (empty range: zeros into a free buffer), so that no branch surrounds
-// them.
+// measured no faster). Between the barriers B_{t-1} and B_t (the one after
+// tile t), group 1 loads V_{t+1} during Y_{t-1} and group 0 loads K_{t+2}
+// during Y_t, while both groups' X_t read K_t and V_{t-1}: every load
+// overwrites a buffer whose last reads (X_{t-1}) ended before B_{t-1}. A wave
+// waits for a tile at the end of the softmax phase before the barrier that
+// precedes the tile's first read, with the tile it has just issued still in
+// flight (vmcnt = one tile's loads). Every softmax phase issues the same
+// loads, also for tiles past the workgroup's last (empty range: zeros into a
+// free buffer), so that no branch surrounds them.
 // MODE: 0 for the method; bit 0 = exact e4m3 rounding of 2^x instead of the
 // Lean P code, bit 1 = no per-block exponent (ablations).
 template <int DQK, int MODE>
@@ -400,12 +402,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     __builtin_amdgcn_s_setprio(0);
   };
   // Y_t: the softmax phase of tile t. ld(u), u = 0..7, issues this wave's
-  // u-th tile load of the slot (or nothing).
+  // u-th tile load of the phase (or nothing).
   auto phase_y = [&](int tt, auto&& ld) {
     // ================= Y_tt: softmax phase
     const int k0 = tt * L::kBK;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) ld(u);  // this slot's tile loads, first
+    for (int u = 0; u < 8; ++u) ld(u);  // this phase's tile loads, first
     __builtin_amdgcn_sched_barrier(0);
     if (k0 + L::kBK - 1 > qw0 + off) {  // the tile crosses this wave's diagonal (or lies past it)
       const int d = qw0 + off - k0 + l32 - 4 * g;
@@ -516,38 +518,36 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   wait_vmem();
   lds_barrier();
 
-  // Each group runs its own copy of the slot loop (2 slots per iteration), so
-  // that S never has to stay live across the loop's back edge in group 0 and
-  // P never in group 1. Both copies execute the same barriers in the same
-  // slots. Every wave runs a softmax phase in every slot of the workgroup's
-  // tile range, also past its own diagonal (all keys masked there) or with
-  // all of its rows past S (never stored): the phase carries the group's
-  // tile loads, and the probabilities it makes are never used.
+  // Each group runs its own copy of the tile loop, so that S never has to
+  // stay live across the loop's back edge in group 0 and P never in group 1.
+  // Both copies execute one barrier per tile. Every wave runs a softmax phase
+  // for every tile of the workgroup's range, also past its own diagonal (all
+  // keys masked there) or with all of its rows past S (never stored): the
+  // phase carries the group's tile loads, and the probabilities it makes are
+  // never used.
   if (grp == 0) {
     for (int t = 0; t <= n_tiles; ++t) {
-      phase_x(t);                              // slot 2t: X_t
-      lds_barrier();
-      if (t < n_tiles) {                       // slot 2t + 1: Y_t, loads K_{t+2}
+      phase_x(t);                              // X_t
+      if (t < n_tiles) {                       // Y_t, loads K_{t+2}
         const auto ldk = k_tile(t + 2);
         phase_y(t, [&](int u) {
           if (u < kKLoads) ldk(u);
         });
-        wait_vmem_all_but<kKLoads>();          // K_{t+1} (loaded in slot 2t-1), first read in slot 2t+2
+        wait_vmem_all_but<kKLoads>();          // K_{t+1} (loaded in Y_{t-1}), first read in X_{t+1}
       }
-      lds_barrier();
+      lds_barrier();                           // B_t
     }
   } else {
     for (int t = 0; t <= n_tiles; ++t) {
-      if (t >= 1) {                            // slot 2t: Y_{t-1}, loads V_{t+1}
+      if (t >= 1) {                            // Y_{t-1}, loads V_{t+1}
         const auto ldv = v_tile(t + 1);
         phase_y(t - 1, [&](int u) {
           if (u < kVLoads) ldv(u);
         });
-        wait_vmem_all_but<kVLoads>();          // V_t (loaded in slot 2t-2), first read in slot 2t+1
+        wait_vmem_all_but<kVLoads>();          // V_t (loaded in Y_{t-2}), first read in X_{t+1}
       }
-      lds_barrier();
-      phase_x(t);                              // slot 2t + 1: X_t
-      lds_barrier();
+      phase_x(t);                              // X_t
+      lds_barrier();                           // B_t
     }
   }
   // the last loads (of tiles past the range) write LDS that the epilogue reuses
