@@ -45,23 +45,41 @@ OTHER_CONFIGS = ["fp8_mla_s32k", "fp8_gqa_s16k_peaked"]
 
 # Sources whose text defines each kernel's code and launch: a stored HBM
 # traffic figure is used only while their hash matches the one recorded with it.
+_COMMON_SOURCES = ["fp8_bf16_causal_amd/csrc/attn_params.h", "fp8_bf16_causal_amd/csrc/attn_common.h",
+                   "fp8_bf16_causal_amd/csrc/attn_launch.h", "fp8_bf16_causal_amd/csrc/attn_api.cpp",
+                   "fp8_bf16_causal_amd/build.py"]
 KERNEL_SOURCES = {
-    "fp8": ["fp8_bf16_causal_amd/csrc/attn_common.h", "fp8_bf16_causal_amd/csrc/attn_api.cpp",
-            "fp8_bf16_causal_amd/csrc/attn_fwd_fp8.hip", "fp8_bf16_causal_amd/build.py"],
-    "bf16": ["fp8_bf16_causal_amd/csrc/attn_common.h", "fp8_bf16_causal_amd/csrc/attn_api.cpp",
-             "fp8_bf16_causal_amd/csrc/attn_fwd_bf16.hip", "fp8_bf16_causal_amd/build.py"],
+    "fp8": _COMMON_SOURCES + ["fp8_bf16_causal_amd/csrc/attn_fwd_fp8.hip"],
+    "bf16": _COMMON_SOURCES + ["fp8_bf16_causal_amd/csrc/attn_fwd_bf16.hip"],
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s32k_hbm_traffic.txt")
 CLOCK_FILE = os.path.join(ROOT, "profiles", "attn_fwd_s32k_mfma_clock_lds.txt")
 
 
+def _code_text(path):
+    """A source file without its comments and blank lines (C/C++ `//` and
+    `/* */` comments, Python `#` comments; these files hold no comment marker
+    inside a string), so that editing a comment keeps the hash."""
+    import re
+
+    with open(path, encoding="utf-8") as f:
+        text = f.read()
+    if path.endswith(".py"):
+        text = re.sub(r"#[^\n]*", "", text)
+    else:
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+    lines = (ln.strip() for ln in text.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def sources_sha256(kind):
+    """Hash of the code (comments left out) of the files a kernel is built from."""
     import hashlib
 
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        h.update(rel.encode() + b"\0" + _code_text(os.path.join(ROOT, rel)).encode() + b"\0")
     return h.hexdigest()
 
 

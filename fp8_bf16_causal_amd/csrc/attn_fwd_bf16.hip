@@ -90,7 +90,9 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(AttnParams p
   const uint8_t* Kg = (const uint8_t*)p.k + (size_t)b * Sk * k_rs + (size_t)kvh * DQK * 2;
   const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * Sk * v_rs + (size_t)kvh * L::kDv * 2;
 
-  // Q^T operand: lane (query l32, half g) holds Q[q][16t + 8g .. +7] per step t.
+  // Q^T operand: lane (query l32, half g) holds Q[q][16t + 8g .. +7] per step t,
+  // loaded from global memory once per wave (no other wave uses these rows, so
+  // an LDS copy would bring no reuse).
   v8bf qf[DQK / 16];
   {
     const int qrow = qw0 + l32;

@@ -64,8 +64,9 @@ constexpr float kLazyLog2 = 8.0f;
 // slot 128 (r / 16) + 16 c + r % 16. Sixteen rows' copies of one chunk are
 // then 256 contiguous bytes (a conflict-free ds_read_b128 for 16 lanes), the
 // reads stay additive in (block, chunk), and a tile is 16 direct-to-LDS
-// instructions, four per wave of the loading group. (At head dim 128 the
-// padded row-major tile measured faster; at 192 this one, by 6%.)
+// instructions, four per wave of the loading group. (At head dim 192
+// this layout measured 6% faster than padded rows; at 128, K uses the
+// swizzled row-major tile below.)
 struct KLoLoader {
   static constexpr int kRegs = 4;
   uint32_t off[kRegs];
@@ -209,7 +210,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   const uint8_t* Vg = (const uint8_t*)p.v + (size_t)b * Sk * v_rs + (size_t)kvh * L::kDv;
 
   // Q^T operand of S^T = K Q^T: lane (query l32, half g) holds, per 64-wide
-  // step t, Q[q][64t + 16g .. +15] and Q[q][64t + 32 + 16g .. +15].
+  // step t, Q[q][64t + 16g .. +15] and Q[q][64t + 32 + 16g .. +15]. Q goes
+  // straight from global memory into these registers, once per wave: each
+  // element is used by one wave only, so staging it in LDS would add a write,
+  // a read and a barrier for no reuse, and the 16-byte loads already read
+  // every 64-byte half-row whole (2 lanes x 2 loads per half-row and step).
   v8i qf[DQK / 64];
   {
     const int qrow = qw0 + l32;

@@ -42,6 +42,28 @@ def test_profile_lines_count_only_for_the_current_sources(tmp_path, monkeypatch)
     assert bench.profiled_line(str(tmp_path / "missing.txt"), "fp8_mha_s32k", "fp8") is None
 
 
+def test_source_hash_ignores_comments_but_not_code(tmp_path, monkeypatch):
+    """Profile figures stay attached to a kernel while only its comments
+    change; any change to the code itself detaches them."""
+    src = tmp_path / "k.hip"
+    py = tmp_path / "b.py"
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setitem(bench.KERNEL_SOURCES, "fp8", ["k.hip", "b.py"])
+
+    def sha(code, build):
+        src.write_text(code)
+        py.write_text(build)
+        return bench.sources_sha256("fp8")
+
+    base = sha("int f(int x) {\n  return x + 1;  // one\n}\n", "FLAGS = ['-O3']  # opt\n")
+    assert base == sha("/* block\n comment */\nint f(int x) {\n\n  return x + 1;  // another\n}\n",
+                       "# header\nFLAGS = ['-O3']\n")
+    assert base != sha("int f(int x) {\n  return x + 2;  // one\n}\n", "FLAGS = ['-O3']  # opt\n")
+    assert base != sha("int f(int x) {\n  return x + 1;  // one\n}\n", "FLAGS = ['-O2']  # opt\n")
+    # a file's code does not leak into its neighbour's: the split point counts
+    assert sha("ab", "c") != sha("a", "bc")
+
+
 def test_balance_bound_of_causal_grids():
     # one workgroup per CU: 4 query heads x 64 blocks of 256 rows at S = 16K;
     # block qb covers 2 qb + 2 key tiles, so the largest load is 128 tiles and
