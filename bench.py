@@ -360,6 +360,7 @@ def sustained(inputs, launch, seconds_warm, seconds_timed):
     for n in inputs:
         p = inputs[n].shape
         kind = inputs[n].dtype
+        ck = ClockSampler()  # set up before the launches: no idle gap in front of the timed ones
         launch(n)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
@@ -372,7 +373,7 @@ def sustained(inputs, launch, seconds_warm, seconds_timed):
         per = (time.perf_counter() - t0) / k
         reps = max(10, int(seconds_timed / per))
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        with ClockSampler() as ck:
+        with ck:
             e0.record()
             for _ in range(reps):
                 launch(n)
@@ -566,6 +567,14 @@ def main():
         ab = dict(exact_p=bool(args.fp8_flags & 1), block_scale=not (args.fp8_flags & 2)) if i.dtype == "fp8" else {}
         fbc.flash_attn_func(i.q, i.k, i.v, i.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n], **ab)
 
+    # everything the timed region needs is set up before the settle and warmup
+    # launches, so that the GPU does not idle (and boost its clock) in front
+    # of the timed steps
+    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+          for n in names}
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    clock = ClockSampler()
+
     # settle the clock: the kernels drive the board to its power limit within
     # seconds, and the clock drops from its idle boost to the sustained one
     t_settle = time.perf_counter()
@@ -579,11 +588,7 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K steps, each kernel bracketed by events on the launch stream
-    ev = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-          for n in names}
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with ClockSampler() as clock:
+    with clock:
         start.record()
         for s in range(args.steps):
             for n in names:

@@ -31,9 +31,10 @@ def _build(tmp_path, compiler, sources, flags, name):
 
 def _run(cmd, env=None):
     e = dict(os.environ)
-    e.pop("LD_PRELOAD", None)
     e.update(env or {})
-    e["ASAN_OPTIONS"] = "detect_leaks=1:abort_on_error=0"
+    # the environment is passed on unchanged; ASan is told not to insist on
+    # being the first library loaded
+    e["ASAN_OPTIONS"] = "detect_leaks=1:abort_on_error=0:verify_asan_link_order=0"
     e["UBSAN_OPTIONS"] = "print_stacktrace=1"
     r = subprocess.run(cmd, capture_output=True, text=True, env=e, timeout=300)
     return r.returncode, r.stdout + r.stderr
