@@ -158,7 +158,7 @@ struct Fp8Layout {
 // instruction stream because the hardware does not track MFMA completion.]
 //
 // Within X_t the operand fragments are read from LDS two MFMA steps ahead (K
-// three at head dim 128) in one ring that runs from the P V steps into the
+// four at head dim 128) in one ring that runs from the P V steps into the
 // Q K steps; the phase starts
 // by reading the first two V fragments (the softmax phase, the longer of the
 // two, then carries no LDS reads of the next tile). Each tile's row sums come
@@ -358,9 +358,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
     // asm definition, no instruction) so it does not occupy registers
     // through the P V half of this phase.
     asm volatile("" : "=v"(s[0]), "=v"(s[1]), "=v"(s[2]), "=v"(s[3]));
-    // Q K fragments are read kKA steps ahead (three at head dim 128; two at
-    // 192, where the registers for a third are not free)
-    constexpr int kKA = DQK == 128 ? 3 : 2;
+    // Q K fragments are read kKA steps ahead (four at head dim 128, where the
+    // K reads meet the other waves' operand reads and the tile copies in the
+    // LDS and need the longer lead; two at 192, where the registers for a
+    // third are not free)
+    constexpr int kKA = DQK == 128 ? 4 : 2;
     constexpr int kKR = kKA + 1;
     v8i kf[kKR];
     v8i q0;  // Q fragment 0 for the Q K steps
