@@ -80,9 +80,6 @@ __device__ inline void map_block(const AttnParams& p, int bid, int& b, int& h, i
 __device__ inline v16f mfma_32x32x64_fp8(v8i a, v8i b, v16f c, int scale_a, int scale_b) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
 }
-__device__ inline v4f mfma_16x16x128_fp8(v8i a, v8i b, v4f c, int scale_a, int scale_b) {
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, scale_b);
-}
 __device__ inline v16f mfma_32x32x16_bf16(v8bf a, v8bf b, v16f c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -263,7 +260,6 @@ __device__ inline int ring_offset(int t, int bytes) {
 }
 
 __device__ inline v4i ld_lds16(const uint8_t* p) { return *(const v4i*)p; }
-__device__ inline void st_lds16(uint8_t* p, v4i x) { *(v4i*)p = x; }
 
 __device__ inline uint32_t pack_bf16(float lo, float hi) {
   v2bf v = {(__bf16)lo, (__bf16)hi};
