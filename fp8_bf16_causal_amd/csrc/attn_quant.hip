@@ -113,7 +113,10 @@ __global__ __launch_bounds__(kQuantThreads) void quant_convert_kernel(const uint
   // q0 = y r is within one ulp of y / s, the remainder y - s q0 is exact
   // (one fma), and q0 + r (y - s q0) rounds to the correctly rounded quotient
   // (Markstein's theorem) as long as nothing underflows, which holds for
-  // s >= 2^-69. Smaller scales take the plain division.
+  // s >= 2^-69. Smaller scales take the plain division. The remainder is
+  // formed as s q0 - y and subtracted: the same value, but for y = -0 the
+  // last step adds -0 to -0 and keeps the quotient's sign (y - s q0 would
+  // turn it into +0).
   const float r = 1.0f / s;
   const bool fast = s >= 0x1p-69f;
   for (int64_t base = wave * kWaveElems; base < n; base += nwaves * kWaveElems) {
@@ -126,8 +129,7 @@ __global__ __launch_bounds__(kQuantThreads) void quant_convert_kernel(const uint
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float q0 = v[i] * r;
-        // (copysign keeps -0: the correction would turn it into +0)
-        q[i] = copysignf(fmaf(fmaf(-q0, s, v[i]), r, q0), v[i]);
+        q[i] = fmaf(-fmaf(q0, s, -v[i]), r, q0);
       }
     } else {
 #pragma unroll
@@ -157,13 +159,19 @@ __global__ __launch_bounds__(kQuantThreads) void quant_convert_kernel(const uint
 constexpr int kHadLaneElems = 32;
 constexpr int kHadWaveElems = 64 * kHadLaneElems;
 
-// The 32 elements of lane `lane` from element e0, as BF16 pairs (elements at
-// or past n read as zeros: whole blocks, as n is a multiple of the block).
+// The 32 elements of lane `lane` from element e0, as BF16 pairs. FULL: the
+// wave's whole step lies below n; else elements at or past n read as zeros
+// (whole lanes, as n is a multiple of the 64-element block).
+template <bool FULL>
 __device__ inline void load32(const uint16_t* x, int64_t e0, int64_t n, qv4i w[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    w[j] = (qv4i){0, 0, 0, 0};
-    if (e0 < n) w[j] = *(const qv4i*)(x + e0 + 8 * j);
+    if constexpr (FULL) {
+      w[j] = *(const qv4i*)(x + e0 + 8 * j);
+    } else {
+      w[j] = (qv4i){0, 0, 0, 0};
+      if (e0 < n) w[j] = *(const qv4i*)(x + e0 + 8 * j);
+    }
   }
 }
 
@@ -212,8 +220,13 @@ __global__ __launch_bounds__(kQuantThreads) void quant_amax_had_kernel(const uin
   float m = 0.0f;
   for (int64_t wbase = wave * 2 * kHadWaveElems; wbase < n; wbase += nwaves * 2 * kHadWaveElems) {
     qv4i w[2][4];
+    if (wbase + 2 * kHadWaveElems <= n) {  // wave-uniform: only the last steps are partial
 #pragma unroll
-    for (int u = 0; u < 2; ++u) load32(x, wbase + u * kHadWaveElems + kHadLaneElems * lane, n, w[u]);
+      for (int u = 0; u < 2; ++u) load32<true>(x, wbase + u * kHadWaveElems + kHadLaneElems * lane, n, w[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) load32<false>(x, wbase + u * kHadWaveElems + kHadLaneElems * lane, n, w[u]);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       float v[32];
@@ -238,13 +251,14 @@ __global__ __launch_bounds__(kQuantThreads) void quant_amax_had_kernel(const uin
 
 // One wave step of the convert pass: rotate, normalise, divide by s, convert,
 // store 32 codes per lane. FAST: y / s from the reciprocal (as in
-// quant_convert_kernel), else the plain division.
-template <int N, bool FAST>
+// quant_convert_kernel), else the plain division. FULL: the whole step lies
+// below n.
+template <int N, bool FAST, bool FULL>
 __device__ inline void convert_had_step(const uint16_t* x, uint8_t* y, int64_t e0, int64_t n, int lane, float s,
                                         float r) {
   const float norm = N == 128 ? 0.08838834764831845f : 0.125f;
   qv4i w[4];
-  load32(x, e0, n, w);
+  load32<FULL>(x, e0, n, w);
   float v[32];
   rotate32<N>(w, lane, v);
 #pragma unroll
@@ -255,7 +269,7 @@ __device__ inline void convert_had_step(const uint16_t* x, uint8_t* y, int64_t e
       const float yv = v[16 * k + i] * norm;
       if constexpr (FAST) {
         const float q0 = yv * r;
-        q[i] = copysignf(fmaf(fmaf(-q0, s, yv), r, q0), yv);
+        q[i] = fmaf(-fmaf(q0, s, -yv), r, q0);
       } else {
         q[i] = yv / s;
       }
@@ -263,10 +277,15 @@ __device__ inline void convert_had_step(const uint16_t* x, uint8_t* y, int64_t e
     qv4i out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i], q[4 * i + 1], 0, false);
+      // the first convert fills the low half of a register whose high half
+      // the second one writes: its old contents do not matter (an empty asm
+      // definition, no instruction)
+      int w;
+      asm volatile("" : "=v"(w));
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i], q[4 * i + 1], w, false);
       out[i] = __builtin_amdgcn_cvt_pk_fp8_f32(q[4 * i + 2], q[4 * i + 3], w, true);
     }
-    if (e0 < n) *(qv4i*)(y + e0 + 16 * k) = out;
+    if (FULL || e0 < n) *(qv4i*)(y + e0 + 16 * k) = out;
   }
 }
 
@@ -280,12 +299,17 @@ __global__ __launch_bounds__(kQuantThreads) void quant_convert_had_kernel(const 
   const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
   const float r = 1.0f / s;
+  // (wbase + step <= n is wave-uniform: only the last steps are partial)
   if (s >= 0x1p-69f) {
-    for (int64_t wbase = wave * kHadWaveElems; wbase < n; wbase += nwaves * kHadWaveElems)
-      convert_had_step<N, true>(x, y, wbase + kHadLaneElems * lane, n, lane, s, r);
+    for (int64_t wbase = wave * kHadWaveElems; wbase < n; wbase += nwaves * kHadWaveElems) {
+      if (wbase + kHadWaveElems <= n)
+        convert_had_step<N, true, true>(x, y, wbase + kHadLaneElems * lane, n, lane, s, r);
+      else
+        convert_had_step<N, true, false>(x, y, wbase + kHadLaneElems * lane, n, lane, s, r);
+    }
   } else {
     for (int64_t wbase = wave * kHadWaveElems; wbase < n; wbase += nwaves * kHadWaveElems)
-      convert_had_step<N, false>(x, y, wbase + kHadLaneElems * lane, n, lane, s, r);
+      convert_had_step<N, false, false>(x, y, wbase + kHadLaneElems * lane, n, lane, s, r);
   }
 }
 

@@ -48,6 +48,8 @@ def test_codes_bit_exact(rows, dim, hadamard):
     x = torch.randn((rows, dim), generator=g) * 3
     x[:, :: max(1, dim // 5)] *= 8.0  # a few outlier channels
     x[0, 0] = -0.0
+    if rows > 1:
+        x[rows - 1] = -0.0  # a whole row of -0: its rotation keeps one -0 per block
     x = x.to(torch.bfloat16)
     _say(f"quantize rows={rows} dim={dim} hadamard={hadamard}")
     codes, sc = run_quant(x, hadamard)
