@@ -27,7 +27,7 @@
 // reduce amax (of the rotated values when rotating) with one vector atomic
 // max per workgroup on the float bits, then (rotate again,) scale and
 // convert. HBM-bound without the rotation, vector-ALU-bound with it (the
-// convert pass spends about 15 instructions per element): 2 reads of the
+// convert pass spends about 14.5 instructions per element): 2 reads of the
 // input, 1 write of the codes.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
