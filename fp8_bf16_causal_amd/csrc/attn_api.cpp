@@ -60,6 +60,10 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
     if (!finite_positive(dq) || !finite_positive(dk) || !finite_positive(dv)) return ATTN_ERR_INVALID;
   }
   if ((flags & ~(unsigned)(ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE)) != 0u) return ATTN_ERR_INVALID;
+  // the base-2 score scale the kernels use, scale dq dk log2(e), must be a
+  // finite float
+  const double cd = (double)scale * dq * dk * kLog2e;
+  if (!(cd <= 3.4e38)) return ATTN_ERR_INVALID;
   // element counts of the largest tensor, whole and per batch entry, checked
   // step by step so that no product itself overflows; the kernels address one
   // batch entry with 32-bit byte offsets (2 bytes per element at most)
@@ -96,7 +100,6 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   p.xcd_group = ((int64_t)B * Hkv) % fbc::kXcds == 0 ? 1 : 0;
   // softmax in base 2: p = 2^((s - m) c). A zero scale (all scores equal) is
   // kept positive so that masked scores (-inf) still map to zero weight.
-  const double cd = (double)scale * dq * dk * kLog2e;
   p.c = (float)(cd > 1e-30 ? cd : 1e-30);
   p.dv = dv;
   p.lse = lse;

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // straight from global memory into these registers, once per wave: each
   // element is used by one wave only, so staging it in LDS would add a write,
   // a read and a barrier for no reuse, and the 16-byte loads already read
-  // every 64-byte half-row whole (2 lanes x 2 loads per half-row and step).
+  // each 64-byte step of a row whole (2 lanes x 2 loads per row and step).
   v8i qf[DQK / 64];
   {
     const int qrow = qw0 + l32;
@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   }
 
   // Each tile goes through a buffer resource that starts at its first key and
-  // ends with key S - 1: rows past the sequence arrive as zeros (finite
+  // ends with key Sk - 1: rows past the sequence arrive as zeros (finite
   // values whose keys every stored query masks). Group 0 (waves 0-3) copies K
   // tiles, group 1 (waves 4-7) V tiles.
   constexpr int kGroupWaves = kWaves / 2;

@@ -76,7 +76,8 @@ enum {
   ATTN_OK = 0,
   /* a null or misaligned pointer (q, k, v, out must be 16-byte aligned), a
    * size <= 0, Hq not a multiple of Hkv, scale negative or not finite, a
-   * descale factor <= 0 or not finite, a flags word with unknown bits, or sizes whose
+   * descale factor <= 0 or not finite, a score scale scale*dq*dk*log2(e)
+   * beyond the float range, a flags word with unknown bits, or sizes whose
    * products overflow the index types (one batch entry of q, k, v or out must
    * stay below 4 GiB; the workgroup count B*Hq*ceil(S/256) below 2^31) */
   ATTN_ERR_INVALID = -1,

@@ -54,6 +54,7 @@ def _call(ptrs=(P, P, P, P), descale=None, flags=0, **kw):
     dict(B=0), dict(S=0), dict(S=-3), dict(Hq=0), dict(Hkv=0), dict(Dqk=0), dict(Dv=-1), dict(Hq=6, Hkv=4),
     dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.1),
     dict(descale=(1.0, 0.0, 1.0)), dict(descale=(1.0, 1.0, float("nan"))), dict(descale=(-1.0, 1.0, 1.0)),
+    dict(scale=3e38, descale=(8.0, 8.0, 1.0)),  # folded score scale beyond the float range
     dict(flags=4), dict(flags=1 << 31), dict(flags=7, dtype=fbc.ATTN_FP8_E4M3),
     dict(B=1 << 20, S=1 << 30, Hq=1 << 10, Hkv=1 << 10), dict(S=1 << 22, Hq=1 << 12, Hkv=1 << 12),
 ])
