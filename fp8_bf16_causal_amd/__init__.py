@@ -1,10 +1,10 @@
 """MI355X (gfx950) causal prefill attention forward: FP8 e4m3 or BF16 inputs,
 BF16 output, through the C-ABI library libfp8_bf16_causal.so.
 
-``attn_fwd`` / ``attn_fwd_ex`` / ``attn_fwd_lse`` / ``attn_fwd_prefix`` / ``attn_quantize_e4m3`` /
-``attn_strerror`` are the C entry points
-(device addresses as ints); ``flash_attn_func`` takes torch tensors. PyTorch
-only provides device memory and the stream.
+``attn_fwd`` / ``attn_fwd_ex`` / ``attn_fwd_lse`` / ``attn_fwd_prefix`` /
+``attn_quantize_e4m3`` / ``attn_strerror`` are the C entry points (device
+addresses as ints); ``flash_attn_func`` and ``quantize_e4m3`` take torch
+tensors. PyTorch only provides device memory and the stream.
 """
 from __future__ import annotations
 
@@ -12,12 +12,12 @@ import math
 
 from . import synth  # noqa: F401
 from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_EXACT_P,
-                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_fwd_lse, attn_fwd_prefix,
-                   attn_quantize_e4m3,
-                   attn_strerror)
+                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_fwd_lse,
+                   attn_fwd_prefix, attn_quantize_e4m3, attn_strerror)
 
-__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_fwd_prefix", "attn_quantize_e4m3", "attn_strerror", "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK",
-           "ATTN_ERR_INVALID", "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
+__all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_fwd_prefix", "attn_quantize_e4m3", "attn_strerror",
+           "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK", "ATTN_ERR_INVALID",
+           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
 
 
 def _raise(code: int):
@@ -33,8 +33,9 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
                     out=None, exact_p=False, block_scale=True, return_lse=False):
     """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
-    factors (ValueError for a factor other than 1 with bfloat16). Returns a new (or the given) bfloat16 tensor [B, S, Hq, Dv],
-    enqueued on the current stream; with return_lse=True, also a float32
+    factors (ValueError for a factor other than 1 with bfloat16). Returns a
+    new (or the given) bfloat16 tensor [B, S, Hq, Dv], enqueued on the
+    current stream; with return_lse=True, also a float32
     tensor [B, Hq, S] of each row's log-sum-exp (attn_fwd_lse). k and v may be
     longer than q (Sk > Sq): the queries are then the last Sq positions and
     query i sees keys j <= i + Sk - Sq (attn_fwd_prefix). exact_p=True /
