@@ -7,7 +7,9 @@ Sk * max(Hq, Hkv) * max(Dqk, Dv) * 2 bytes against 2^32. With 255 heads of
 limit (BF16 tensors of exactly that size; FP8 tensors of half of it), so the
 last head's last rows sit at offsets within 16 MiB of 2^32. Sampled rows of
 the first and last heads are compared with the fp64 oracle at the parity
-bars; 256 heads (exactly 2^32 bytes) are refused on the host.
+bars; 256 heads (exactly 2^32 bytes) are refused on the host. A second case
+has two batch entries of 2 GiB each (BF16, 128 heads), so the second entry
+starts past 2^31 and its last rows end near 2^32 bytes into each tensor.
 """
 import math
 import sys
@@ -38,12 +40,13 @@ def _say(msg):
     sys.stdout.flush()
 
 
-def _tensor(g, dtype):
-    """[1, S, H, D] N(0, 1) values in dtype, made 4,096 rows at a time."""
-    t = torch.empty((1, S, H, D), dtype=dtype, device="cuda")
-    for r in range(0, S, 4096):
-        x = torch.randn((1, 4096, H, D), generator=g, device="cuda", dtype=torch.float32)
-        t[:, r:r + 4096] = x.to(dtype)
+def _tensor(g, dtype, B=1, heads=H):
+    """[B, S, heads, D] N(0, 1) values in dtype, made 4,096 rows at a time."""
+    t = torch.empty((B, S, heads, D), dtype=dtype, device="cuda")
+    for b in range(B):
+        for r in range(0, S, 4096):
+            x = torch.randn((4096, heads, D), generator=g, device="cuda", dtype=torch.float32)
+            t[b, r:r + 4096] = x.to(dtype)
     return t
 
 
@@ -54,30 +57,31 @@ def test_refuses_a_batch_entry_of_four_gib():
     assert rc == fbc.ATTN_ERR_INVALID
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_largest_accepted_tensors(dtype):
+@pytest.mark.parametrize("dtype,B,heads", [("bf16", 1, H), ("fp8", 1, H), ("bf16", 2, 128)])
+def test_largest_accepted_tensors(dtype, B, heads):
     import fp8_bf16_causal_amd as fbc
-    _say(f"case max size {dtype} S={S} H={H} D={D}")
+    _say(f"case max size {dtype} B={B} S={S} H={heads} D={D}")
     torch.cuda.empty_cache()
-    g = torch.Generator(device="cuda").manual_seed(11 if dtype == "bf16" else 12)
+    g = torch.Generator(device="cuda").manual_seed(11 + B + (dtype == "fp8"))
     tdt = torch.bfloat16 if dtype == "bf16" else torch.float8_e4m3fn
-    q, k, v = (_tensor(g, tdt) for _ in range(3))
-    out = torch.empty((1, S, H, D), dtype=torch.bfloat16, device="cuda")
+    q, k, v = (_tensor(g, tdt, B, heads) for _ in range(3))
+    out = torch.empty((B, S, heads, D), dtype=torch.bfloat16, device="cuda")
     scale = 1.0 / math.sqrt(D)
     dt = fbc.ATTN_BF16 if dtype == "bf16" else fbc.ATTN_FP8_E4M3
     torch.cuda.synchronize()
-    rc = fbc.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), 1, H, H, S, D, D, 1, scale, dt,
-                         None, None, 0)
+    rc = fbc.attn_fwd_ex(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, heads, heads, S, D, D, 1, scale,
+                         dt, None, None, 0)
     assert rc == fbc.ATTN_OK, fbc.attn_strerror(rc)
     torch.cuda.synchronize()
-    heads = [0, H - 1]
+    bl = B - 1  # the last batch entry
+    hs = [0, heads - 1]
     rows_i = [0, 1, 127, 128, 4095, 32768, S - 129, S - 2, S - 1]
-    sub = [t[:, :, heads].contiguous() for t in (q, k, v)]
-    rows = np.array([(0, j, i) for j in range(len(heads)) for i in rows_i], dtype=np.int64)
+    sub = [t[bl:bl + 1, :, hs].contiguous() for t in (q, k, v)]
+    rows = np.array([(0, j, i) for j in range(len(hs)) for i in rows_i], dtype=np.int64)
     odt = oracle.BF16 if dtype == "bf16" else oracle.FP8_E4M3
     ref = oracle.attention(synth.raw_codes(sub[0]), synth.raw_codes(sub[1]), synth.raw_codes(sub[2]), odt, scale,
                            rows=rows)
-    got = np.stack([out[0, i, heads[j]].float().cpu().numpy() for (_, j, i) in rows]).astype(np.float64)
+    got = np.stack([out[bl, i, hs[j]].float().cpu().numpy() for (_, j, i) in rows]).astype(np.float64)
     vmax = float(np.max(np.abs(oracle.dequantize(synth.raw_codes(sub[2]), odt, 1.0))))
     del q, k, v, out, sub
     torch.cuda.empty_cache()
