@@ -120,3 +120,43 @@ def test_rotation_lowers_fp8_attention_error_on_peaked_inputs():
     # the pages: the rotation roughly halves the input-quantisation error (here the
     # sink and outlier channels make the per-tensor scale coarse without it)
     assert err[True] < 0.5 * err[False]
+
+
+@pytest.mark.parametrize("hadamard", [False, True])
+def test_more_than_two_to_the_31_elements(hadamard):
+    """2^31 + 2^20 elements in 128-element rows, so element indices pass 2^31:
+    noise in [-1/16, 1/16] and one spike of 100 in a row past 2^31. The
+    spike's block holds the tensor's amax with and without the rotation (any
+    other rotated value is below 0.71, the spike's block's above 8.1), so the
+    oracle run on that row together with sampled rows (the first, around 2^31,
+    the last) decides the same scale, and every sampled code must agree."""
+    import fp8_bf16_causal_amd as fbc
+    dim = 128
+    n = (1 << 31) + (1 << 20)
+    rows = n // dim
+    _say(f"quantize {n} elements hadamard={hadamard}")
+    x = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(77)
+    chunk = 1 << 26
+    for o in range(0, n, chunk):
+        m = min(chunk, n - o)
+        x[o:o + m] = ((torch.rand(m, generator=g, device="cuda") - 0.5) * 0.125).to(torch.bfloat16)
+    r31 = (1 << 31) // dim
+    spike_row = r31 + 1234
+    x[spike_row * dim + 37] = 100.0
+    y = torch.empty(n, dtype=torch.uint8, device="cuda")
+    sc = torch.empty(2, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = fbc.attn_quantize_e4m3(x.data_ptr(), y.data_ptr(), sc.data_ptr(), rows, dim, int(hadamard), stream)
+    assert rc == fbc.ATTN_OK, fbc.attn_strerror(rc)
+    torch.cuda.synchronize()
+    sample = [0, 1, r31 - 1, r31, r31 + 1, spike_row, rows - 2, rows - 1]
+    xs = torch.stack([x[r * dim:(r + 1) * dim] for r in sample]).cpu()
+    got = torch.stack([y[r * dim:(r + 1) * dim] for r in sample]).cpu().numpy()
+    scv = sc.cpu().numpy()
+    del x, y
+    torch.cuda.empty_cache()
+    ref, s, amax = quant.quantize_e4m3(bits(xs), hadamard)
+    assert scv[1] == amax and scv[0] == s
+    mism = int(np.sum(got != ref))
+    assert mism == 0, f"{mism} codes differ"
