@@ -19,7 +19,9 @@
  *   - layout is flash_attn_func's (batch, seq, heads, dim), contiguous;
  *   - grouped-query attention: query head h reads KV head h / (Hq / Hkv);
  *   - causal mask with equal query and key lengths: key j is visible to row i
- *     iff j <= i;
+ *     iff j <= i; with Sk > Sq keys the queries are the last Sq positions, so
+ *     key j is visible to query i iff j <= i + Sk - Sq (flash_attn_func's
+ *     alignment; oracle_attn_prefix_f64);
  *   - FP8 inputs carry one per-tensor dequantisation factor each (dq, dk, dv):
  *     the score scale becomes scale*dq*dk and dv multiplies the output.
  *
@@ -28,9 +30,11 @@
  * the weighted V sum are all double. No tiling, no online rescaling: each row
  * is the textbook softmax over its visible keys.
  *
- * Parity pins (tests/test_oracle.py): brute force on tiny inputs; a library
- * routine (torch scaled_dot_product_attention, float64, causal); closed forms
- * (row 0 equals V[0]; equal scores give the prefix mean of V); invariants
+ * Parity pins (tests/test_oracle.py): brute force on tiny inputs (outputs,
+ * log-sum-exp, the probability matrix of oracle_attn_probs_f64, queries after
+ * a key prefix); a library routine (torch scaled_dot_product_attention,
+ * float64, causal, and with an explicit bottom-right mask); closed forms (row
+ * 0 equals V[0]; equal scores give the prefix mean of V); invariants
  * (probability rows sum to one, score shift invariance, GQA equals MHA with
  * repeated K/V, V column permutation); decoders against torch's casts on all
  * codes.
