@@ -350,6 +350,46 @@ def test_runs_on_a_side_stream():
     check(inp, out, oracle_out(inp), "fp8 side stream")
 
 
+def test_concurrent_calls_from_host_threads_on_separate_streams():
+    """The library keeps no state between calls (the device check is cached
+    in an atomic): eight host threads, each with its own stream and its own
+    inputs (both dtypes, several shapes), call it at the same time, twenty
+    times each; every result equals the same call made alone, bit for bit."""
+    import threading
+
+    import fp8_bf16_causal_amd as fbc
+    cases = []
+    for t in range(8):
+        dtype = "fp8" if t % 2 else "bf16"
+        inp = synth.make_inputs(B=1 + t % 2, S=200 + 97 * t, Hq=4, Hkv=2 if t % 3 else 4, Dqk=192 if t == 5 else 128,
+                                Dv=128, dtype=dtype, seed=100 + t, device="cuda")
+        alone = run_gpu(inp).clone()
+        cases.append((inp, alone))
+    errors = []
+
+    def work(i):
+        inp, alone = cases[i]
+        dq, dk, dv = inp.descale
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            outs = [fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv)
+                    for _ in range(20)]
+        s.synchronize()
+        for o in outs:
+            if not torch.equal(o.view(torch.int16), alone.view(torch.int16)):
+                errors.append(i)
+                break
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(len(cases))]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    _say(f"concurrent host threads: {len(cases)} x 20 calls, mismatching cases {errors}")
+    assert not errors
+
+
 # ------------------------------------------------------------------ full benchmark shapes, sampled rows
 
 def sample_rows(B, S, Hq, n_random, seed):
