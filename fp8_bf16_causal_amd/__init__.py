@@ -11,13 +11,14 @@ from __future__ import annotations
 import math
 
 from . import synth  # noqa: F401
-from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_EXACT_P,
-                   ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex, attn_fwd_lse,
-                   attn_fwd_prefix, attn_quantize_e4m3, attn_strerror)
+from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPPORTED, ATTN_FLAG_DESCALE_DEVICE,
+                   ATTN_FLAG_EXACT_P, ATTN_FLAG_NO_BLOCKSCALE, ATTN_FP8_E4M3, ATTN_OK, attn_fwd, attn_fwd_ex,
+                   attn_fwd_lse, attn_fwd_prefix, attn_quantize_e4m3, attn_strerror)
 
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_fwd_prefix", "attn_quantize_e4m3", "attn_strerror",
            "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK", "ATTN_ERR_INVALID",
-           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE"]
+           "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE",
+           "ATTN_FLAG_DESCALE_DEVICE"]
 
 
 def _raise(code: int):
@@ -30,7 +31,7 @@ def _raise(code: int):
 
 
 def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, descale_k=None, descale_v=None,
-                    out=None, exact_p=False, block_scale=True, return_lse=False):
+                    out=None, exact_p=False, block_scale=True, return_lse=False, descale_device=None):
     """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
     factors (ValueError for a factor other than 1 with bfloat16). Returns a
@@ -40,7 +41,11 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     longer than q (Sk > Sq): the queries are then the last Sq positions and
     query i sees keys j <= i + Sk - Sq (attn_fwd_prefix). exact_p=True /
     block_scale=False select the FP8 softmax ablations (ATTN_FLAG_EXACT_P /
-    ATTN_FLAG_NO_BLOCKSCALE)."""
+    ATTN_FLAG_NO_BLOCKSCALE). descale_device: instead of descale_q/k/v, a
+    contiguous float32 tensor on q's device holding {dq, amax_q, dk, amax_k,
+    dv, amax_v} (three quantize_e4m3 calls with scale_out=buf[0:2], buf[2:4],
+    buf[4:6]), read by the kernels: no host round trip
+    (ATTN_FLAG_DESCALE_DEVICE)."""
     import torch
 
     if q.dtype == torch.bfloat16:
@@ -75,6 +80,14 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     if dtype == ATTN_FP8_E4M3 and any(x is not None for x in (descale_q, descale_k, descale_v)):
         ds = tuple(1.0 if x is None else float(x) for x in (descale_q, descale_k, descale_v))
     flags = (ATTN_FLAG_EXACT_P if exact_p else 0) | (0 if block_scale else ATTN_FLAG_NO_BLOCKSCALE)
+    if descale_device is not None:
+        if dtype != ATTN_FP8_E4M3 or ds is not None:
+            raise ValueError("descale_device goes with float8_e4m3fn inputs and no descale_q/k/v")
+        if (descale_device.dtype != torch.float32 or descale_device.device != q.device
+                or not descale_device.is_contiguous() or descale_device.numel() < 5):
+            raise ValueError("descale_device must be a contiguous float32 tensor of 6 values on q's device")
+        ds = descale_device.data_ptr()
+        flags |= ATTN_FLAG_DESCALE_DEVICE
     stream = torch.cuda.current_stream(q.device).cuda_stream
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device) if return_lse else None
     with torch.cuda.device(q.device):
@@ -93,11 +106,13 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     return (out, lse) if return_lse else out
 
 
-def quantize_e4m3(x, hadamard=False):
+def quantize_e4m3(x, hadamard=False, scale_out=None):
     """Per-tensor e4m3fn quantisation of a bfloat16 tensor [..., dim] on the
     GPU (dim 64, 128, 192 or 256), optionally rotating each row by a Hadamard
     transform first (for Q and K). Returns (codes as float8_e4m3fn, a device
     float32 tensor [s, amax]); attn_fwd takes the codes with descale s.
+    scale_out: optional contiguous float32 device tensor of 2 values to write
+    [s, amax] into (e.g. a slice of flash_attn_func's descale_device buffer).
     Enqueued on the current stream."""
     import torch
 
@@ -106,7 +121,13 @@ def quantize_e4m3(x, hadamard=False):
     dim = x.shape[-1]
     rows = x.numel() // dim if dim else 0
     y = torch.empty(x.shape, dtype=torch.float8_e4m3fn, device=x.device)
-    scale = torch.empty(2, dtype=torch.float32, device=x.device)
+    if scale_out is None:
+        scale = torch.empty(2, dtype=torch.float32, device=x.device)
+    else:
+        if (scale_out.dtype != torch.float32 or scale_out.device != x.device or not scale_out.is_contiguous()
+                or scale_out.numel() != 2):
+            raise ValueError("scale_out must be a contiguous float32 tensor of 2 values on x's device")
+        scale = scale_out
     stream = torch.cuda.current_stream(x.device).cuda_stream
     with torch.cuda.device(x.device):
         rc = attn_quantize_e4m3(x.data_ptr(), y.data_ptr(), scale.data_ptr(), rows, dim, 1 if hadamard else 0, stream)

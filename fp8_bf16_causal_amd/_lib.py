@@ -14,6 +14,7 @@ ATTN_ERR_UNSUPPORTED = -2
 ATTN_ERR_LAUNCH = -3
 ATTN_FLAG_EXACT_P = 1
 ATTN_FLAG_NO_BLOCKSCALE = 2
+ATTN_FLAG_DESCALE_DEVICE = 4
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfp8_bf16_causal.so")
 _lib = None
@@ -32,14 +33,13 @@ def load():
     vp, i32, f32, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32]
     lib.attn_fwd.restype = i32
-    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                ctypes.POINTER(ctypes.c_float), vp, u32]
+    # descale_qkv: a host float[3] or, with ATTN_FLAG_DESCALE_DEVICE, a device address
+    lib.attn_fwd_ex.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, u32]
     lib.attn_fwd_ex.restype = i32
-    lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                 ctypes.POINTER(ctypes.c_float), vp, u32]
+    lib.attn_fwd_lse.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp, u32]
     lib.attn_fwd_lse.restype = i32
-    lib.attn_fwd_prefix.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32,
-                                    ctypes.POINTER(ctypes.c_float), vp, u32]
+    lib.attn_fwd_prefix.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, vp,
+                                    u32]
     lib.attn_fwd_prefix.restype = i32
     lib.attn_quantize_e4m3.argtypes = [vp, vp, vp, ctypes.c_longlong, i32, i32, vp]
     lib.attn_quantize_e4m3.restype = i32
@@ -49,6 +49,17 @@ def load():
     return lib
 
 
+def _descale(descale_qkv, flags):
+    """The descale_qkv argument: None; a device address (int) with
+    ATTN_FLAG_DESCALE_DEVICE; else three host floats, as a float[3] that the
+    caller keeps alive through the call."""
+    if descale_qkv is None:
+        return None
+    if flags & ATTN_FLAG_DESCALE_DEVICE:
+        return ctypes.c_void_p(int(descale_qkv))
+    return (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
+
+
 def attn_fwd(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype) -> int:
     """q, k, v, out: device addresses (ints). Returns the library's code."""
     return load().attn_fwd(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype)
@@ -56,19 +67,16 @@ def attn_fwd(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype) -> int:
 
 def attn_fwd_ex(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv=None, stream=None,
                 flags=0) -> int:
-    """descale_qkv: (dq, dk, dv) or None; stream: a hipStream_t as int, or None."""
-    ds = None
-    if descale_qkv is not None:
-        ds = (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
+    """descale_qkv: (dq, dk, dv), a device address with ATTN_FLAG_DESCALE_DEVICE,
+    or None; stream: a hipStream_t as int, or None."""
+    ds = _descale(descale_qkv, flags)
     return load().attn_fwd_ex(q, k, v, out, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, ds, stream, flags)
 
 
 def attn_fwd_lse(q, k, v, out, lse, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, descale_qkv=None, stream=None,
                  flags=0) -> int:
     """attn_fwd_ex plus lse: the device address of B*Hq*S float32 log-sum-exps."""
-    ds = None
-    if descale_qkv is not None:
-        ds = (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
+    ds = _descale(descale_qkv, flags)
     return load().attn_fwd_lse(q, k, v, out, lse, B, Hq, Hkv, S, Dqk, Dv, causal, scale, dtype, ds, stream, flags)
 
 
@@ -76,9 +84,7 @@ def attn_fwd_prefix(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, Dqk, Dv, causal, scal
                     stream=None, flags=0) -> int:
     """Sq queries (the last Sq positions) over Sk >= Sq keys; lse: device
     address of B*Hq*Sq float32 or None."""
-    ds = None
-    if descale_qkv is not None:
-        ds = (ctypes.c_float * 3)(*[float(x) for x in descale_qkv])
+    ds = _descale(descale_qkv, flags)
     return load().attn_fwd_prefix(q, k, v, out, lse, B, Hq, Hkv, Sq, Sk, Dqk, Dv, causal, scale, dtype, ds, stream,
                                   flags)
 

@@ -52,16 +52,21 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || S <= 0 || Sk < S || Dqk <= 0 || Dv <= 0) return ATTN_ERR_INVALID;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID;
   if (!std::isfinite(scale) || scale < 0.0f) return ATTN_ERR_INVALID;
+  const unsigned known = ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE | ATTN_FLAG_DESCALE_DEVICE;
+  if ((flags & ~known) != 0u) return ATTN_ERR_INVALID;
+  // device-resident factors are read by the kernels; host ones here
+  const bool dev_descale = (flags & ATTN_FLAG_DESCALE_DEVICE) != 0u;
   float dq = 1.0f, dk = 1.0f, dv = 1.0f;
-  if (descale_qkv) {
+  if (dev_descale) {
+    if (!descale_qkv || ((uintptr_t)descale_qkv & 3u)) return ATTN_ERR_INVALID;
+  } else if (descale_qkv) {
     dq = descale_qkv[0];
     dk = descale_qkv[1];
     dv = descale_qkv[2];
     if (!finite_positive(dq) || !finite_positive(dk) || !finite_positive(dv)) return ATTN_ERR_INVALID;
   }
-  if ((flags & ~(unsigned)(ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE)) != 0u) return ATTN_ERR_INVALID;
   // the base-2 score scale the kernels use, scale dq dk log2(e), must be a
-  // finite float
+  // finite float (for device factors only the host part can be checked)
   const double cd = (double)scale * dq * dk * kLog2e;
   if (!(cd <= 3.4e38)) return ATTN_ERR_INVALID;
   // element counts of the largest tensor, whole and per batch entry, checked
@@ -102,11 +107,14 @@ static int attn_fwd_impl(const void* q, const void* k, const void* v, void* out,
   // kept positive so that masked scores (-inf) still map to zero weight.
   p.c = (float)(cd > 1e-30 ? cd : 1e-30);
   p.dv = dv;
+  p.scale = scale;
+  p.dscale = dev_descale ? descale_qkv : nullptr;
   p.lse = lse;
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();  // clear a stale error so the launch check below is ours
-  const hipError_t e = dtype == ATTN_FP8_E4M3 ? fbc::launch_attn_fwd_fp8(p, Dqk, (int)flags, (int)grid, st)
+  const int mode = (int)(flags & (ATTN_FLAG_EXACT_P | ATTN_FLAG_NO_BLOCKSCALE));
+  const hipError_t e = dtype == ATTN_FP8_E4M3 ? fbc::launch_attn_fwd_fp8(p, Dqk, mode, (int)grid, st)
                                               : fbc::launch_attn_fwd_bf16(p, Dqk, (int)grid, st);
   return e == hipSuccess ? ATTN_OK : ATTN_ERR_LAUNCH;
 }

@@ -333,6 +333,14 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // the base-2 score scale lives in a vector register: as a scalar it would be
   // spilled and reloaded every tile under this kernel's scalar-register pressure
   float c = p.c;
+  float dv = p.dv;
+  if (p.dscale != nullptr) {
+    // dequantisation factors left on the device by the quantize prologue:
+    // folded in the same precision and order as the host folds its own
+    const double cd = (double)p.scale * p.dscale[0] * p.dscale[2] * 1.4426950408889634;
+    c = (float)(cd > 1e-30 ? cd : 1e-30);
+    dv = p.dscale[4];
+  }
   asm volatile("" : "+v"(c));
   const float c8 = 8.0f * c;
 
@@ -564,7 +572,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_fp8_kernel(AttnParams p)
   // ---- epilogue: O / l * dv -> BF16, staged through LDS for coalesced rows.
   uint8_t* Ol = lds + wave * kQW * kOStride;
   if (wave_tiles > 0) {
-    const float inv = p.dv / l;
+    const float inv = dv / l;
     // log-sum-exp of the row's logits: sum_j 2^(c s_j) = 2^(c m) l
     if (p.lse != nullptr && g == 0 && qw0 + l32 < S)
       p.lse[((size_t)b * p.Hq + h) * S + qw0 + l32] = (m * c + __builtin_amdgcn_logf(l)) * kLn2;

@@ -24,8 +24,11 @@ struct AttnParams {
   int G;          // Hq / Hkv
   int nqb;        // query blocks per head, ceil(S / kBQ)
   int xcd_group;  // 1: every KV head's workgroups run on one XCD
-  float c;        // softmax scale * dq * dk * log2(e) (> 0)
+  float c;        // softmax scale * dq * dk * log2(e) (> 0), folded on the host
   float dv;       // output dequantisation factor
+  float scale;    // softmax scale (for factors read on the device)
+  const float* dscale;  // NULL, or device {dq, amax_q, dk, amax_k, dv, amax_v}: the
+                        // kernel folds dq, dk and reads dv itself, as the host does
   float* lse;     // NULL, or [B][Hq][S]: each row's log-sum-exp of its logits
 };
 

@@ -71,13 +71,30 @@ enum { ATTN_BF16 = 0, ATTN_FP8_E4M3 = 1 };
  */
 enum { ATTN_FLAG_EXACT_P = 1u, ATTN_FLAG_NO_BLOCKSCALE = 2u };
 
+/*
+ * ATTN_FLAG_DESCALE_DEVICE (dtype ATTN_FP8_E4M3 only; combines with the
+ * ablation flags): descale_qkv is a device pointer (4-byte aligned) to six
+ * floats {dq, amax_q, dk, amax_k, dv, amax_v}, the layout three
+ * attn_quantize_e4m3 calls produce when their scale buffers lie back to back
+ * (scale, scale + 2, scale + 4). The kernels read dq, dk and dv at launch, so
+ * a caller can quantise Q, K and V and run the attention on one stream, or in
+ * one graph, with no host round trip. The factors are not validated (a
+ * quantize call always writes finite positive ones); the score scale is folded
+ * exactly as for host factors, so the output is bit-identical to a call with
+ * the same values passed from the host. Reading the pages: the factors are the
+ * per-tensor scales of the quantisation step [spbcomputers.ru ZYFA article,
+ * section "Точность: ошибка FP8 ниже, чем у AITER"].
+ */
+enum { ATTN_FLAG_DESCALE_DEVICE = 4u };
+
 /* Return codes. */
 enum {
   ATTN_OK = 0,
   /* a null or misaligned pointer (q, k, v, out must be 16-byte aligned), a
    * size <= 0, Hq not a multiple of Hkv, scale negative or not finite, a
    * descale factor <= 0 or not finite, a score scale scale*dq*dk*log2(e)
-   * beyond the float range, a flags word with unknown bits, or sizes whose
+   * beyond the float range, a flags word with unknown bits, a null or
+   * misaligned descale_qkv with ATTN_FLAG_DESCALE_DEVICE, or sizes whose
    * products overflow the index types (one batch entry of q, k, v or out must
    * stay below 4 GiB; the workgroup count B*Hq*ceil(S/256) below 2^31) */
   ATTN_ERR_INVALID = -1,
@@ -107,10 +124,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
  * attn_fwd_ex: attn_fwd with per-tensor dequantisation factors and a stream.
  *
  *   descale_qkv  host pointer to {dq, dk, dv}, or NULL for {1, 1, 1}; read
- *                during the call only
+ *                during the call only (with ATTN_FLAG_DESCALE_DEVICE: a device
+ *                pointer to six floats, read by the kernels, see above)
  *   stream       a hipStream_t, or NULL for the null stream
- *   flags        0, or ATTN_FLAG_* bits (FP8 only) selecting an ablation of
- *                the FP8 softmax
+ *   flags        0, or ATTN_FLAG_* bits (FP8 only): ablations of the FP8
+ *                softmax, device-resident dequantisation factors
  */
 int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, int Hq, int Hkv, int S, int Dqk,
                 int Dv, int causal, float scale, int dtype, const float* descale_qkv, void* stream,

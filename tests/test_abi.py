@@ -55,7 +55,10 @@ def _call(ptrs=(P, P, P, P), descale=None, flags=0, **kw):
     dict(scale=float("nan")), dict(scale=float("inf")), dict(scale=-0.1),
     dict(descale=(1.0, 0.0, 1.0)), dict(descale=(1.0, 1.0, float("nan"))), dict(descale=(-1.0, 1.0, 1.0)),
     dict(scale=3e38, descale=(8.0, 8.0, 1.0)),  # folded score scale beyond the float range
-    dict(flags=4), dict(flags=1 << 31), dict(flags=7, dtype=fbc.ATTN_FP8_E4M3),
+    dict(flags=8), dict(flags=1 << 31), dict(flags=15, dtype=fbc.ATTN_FP8_E4M3),
+    # device-resident descales: a null or misaligned pointer
+    dict(flags=fbc.ATTN_FLAG_DESCALE_DEVICE, dtype=fbc.ATTN_FP8_E4M3),
+    dict(flags=fbc.ATTN_FLAG_DESCALE_DEVICE, dtype=fbc.ATTN_FP8_E4M3, descale=P + 2),
     dict(B=1 << 20, S=1 << 30, Hq=1 << 10, Hkv=1 << 10), dict(S=1 << 22, Hq=1 << 12, Hkv=1 << 12),
 ])
 def test_invalid_arguments(kw):
@@ -65,6 +68,7 @@ def test_invalid_arguments(kw):
 @pytest.mark.parametrize("kw", [
     dict(causal=0), dict(dtype=2), dict(dtype=-1), dict(Dqk=64, Dv=64), dict(Dqk=128, Dv=64), dict(Dqk=256, Dv=256),
     dict(flags=fbc.ATTN_FLAG_EXACT_P), dict(flags=fbc.ATTN_FLAG_NO_BLOCKSCALE),  # the ablations are FP8-only
+    dict(flags=fbc.ATTN_FLAG_DESCALE_DEVICE, descale=P),  # device-resident descales too
 ])
 def test_unsupported_arguments(kw):
     assert _call(**kw) == fbc.ATTN_ERR_UNSUPPORTED

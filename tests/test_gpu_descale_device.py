@@ -1,0 +1,100 @@
+"""GPU: FP8 prefill from BF16 tensors with no host round trip. Q and K are
+quantised with the Hadamard rotation and V without, by attn_quantize_e4m3,
+into one device buffer {dq, amax_q, dk, amax_k, dv, amax_v}; the attention
+reads its dequantisation factors from that buffer (ATTN_FLAG_DESCALE_DEVICE).
+The output must equal, bit for bit, the same call with the factors read back
+and passed from the host, and meet the FP8 bar against the oracle; and the
+whole chain (three quantize calls and the attention) captured in a HIP graph
+must follow new input values on every replay, scales included."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from fp8_bf16_causal_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import fp8_bf16_causal_amd._lib as L
+    L.load()
+    torch.cuda.set_device(0)
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _bf16_inputs(seed, B=1, S=1000, Hq=4, Hkv=2, D=128):
+    inp = synth.make_inputs(B=B, S=S, Hq=Hq, Hkv=Hkv, Dqk=D, Dv=D, dtype="bf16", seed=seed, structure="peaked",
+                            device="cuda")
+    return inp.q, inp.k, inp.v, inp.scale
+
+
+def _chain(q, k, v, scale, buf):
+    """Quantise (rotating Q and K) into buf, then attention with device factors."""
+    import fp8_bf16_causal_amd as fbc
+    q8, _ = fbc.quantize_e4m3(q, hadamard=True, scale_out=buf[0:2])
+    k8, _ = fbc.quantize_e4m3(k, hadamard=True, scale_out=buf[2:4])
+    v8, _ = fbc.quantize_e4m3(v, hadamard=False, scale_out=buf[4:6])
+    out = fbc.flash_attn_func(q8, k8, v8, scale, descale_device=buf)
+    return q8, k8, v8, out
+
+
+def test_device_factors_equal_host_factors_and_meet_the_bar():
+    import fp8_bf16_causal_amd as fbc
+    q, k, v, scale = _bf16_inputs(61)
+    buf = torch.empty(6, dtype=torch.float32, device="cuda")
+    q8, k8, v8, out_dev = _chain(q, k, v, scale, buf)
+    torch.cuda.synchronize()
+    dq, _, dk, _, dv, _ = [float(x) for x in buf.cpu()]
+    out_host = fbc.flash_attn_func(q8, k8, v8, scale, descale_q=dq, descale_k=dk, descale_v=dv)
+    torch.cuda.synchronize()
+    assert torch.equal(out_dev.view(torch.int16), out_host.view(torch.int16))
+    ref = oracle.attention(synth.raw_codes(q8), synth.raw_codes(k8), synth.raw_codes(v8), oracle.FP8_E4M3, scale,
+                           dq, dk, dv)
+    got = out_dev.float().cpu().numpy().astype(np.float64)
+    err = got - ref
+    rel = math.sqrt(float(np.sum(err ** 2)) / float(np.sum(ref ** 2)))
+    vmax = float(np.max(np.abs(oracle.dequantize(synth.raw_codes(v8), oracle.FP8_E4M3, dv))))
+    _say(f"device factors dq={dq:.4g} dk={dk:.4g} dv={dv:.4g}: rel_rms={rel:.3e} maxabs={np.max(np.abs(err)):.3e}")
+    assert rel <= 4e-2 and float(np.max(np.abs(err))) <= 0.1 * vmax
+
+
+def test_chain_in_a_graph_follows_new_inputs():
+    q, k, v, scale = _bf16_inputs(62)
+    sq, sk, sv = (t.clone() for t in (q, k, v))  # static inputs of the graph
+    buf = torch.empty(6, dtype=torch.float32, device="cuda")
+    _chain(sq, sk, sv, scale, buf)  # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _, _, _, gout = _chain(sq, sk, sv, scale, buf)
+    torch.cuda.synchronize()
+    for r in range(3):
+        nq, nk, nv, _ = _bf16_inputs(70 + r)
+        amp = 0.25 * (r + 1)  # new magnitudes: the factors must change too
+        sq.copy_(nq * amp)
+        sk.copy_(nk)
+        sv.copy_(nv * (4.0 - r))
+        gout.fill_(float("nan"))
+        buf.fill_(-1.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = gout.clone()
+        got_buf = buf.clone()
+        ebuf = torch.empty(6, dtype=torch.float32, device="cuda")
+        _, _, _, eout = _chain(sq, sk, sv, scale, ebuf)
+        torch.cuda.synchronize()
+        same = torch.equal(got.view(torch.int16), eout.view(torch.int16)) and torch.equal(got_buf, ebuf)
+        _say(f"replay {r}: factors {[round(float(x), 5) for x in got_buf.cpu()[0::2]]} identical to eager {same}")
+        assert same
