@@ -85,7 +85,8 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
             raise ValueError("descale_device goes with float8_e4m3fn inputs and no descale_q/k/v")
         if (descale_device.dtype != torch.float32 or descale_device.device != q.device
                 or not descale_device.is_contiguous() or descale_device.numel() < 5):
-            raise ValueError("descale_device must be a contiguous float32 tensor of 6 values on q's device")
+            raise ValueError("descale_device must be a contiguous float32 tensor on q's device holding at least "
+                             "{dq, amax_q, dk, amax_k, dv} (the kernels read elements 0, 2 and 4)")
         ds = descale_device.data_ptr()
         flags |= ATTN_FLAG_DESCALE_DEVICE
     stream = torch.cuda.current_stream(q.device).cuda_stream

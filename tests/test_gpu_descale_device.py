@@ -98,3 +98,41 @@ def test_chain_in_a_graph_follows_new_inputs():
         same = torch.equal(got.view(torch.int16), eout.view(torch.int16)) and torch.equal(got_buf, ebuf)
         _say(f"replay {r}: factors {[round(float(x), 5) for x in got_buf.cpu()[0::2]]} identical to eager {same}")
         assert same
+
+
+@pytest.mark.parametrize("flags", [0, 1, 2, 3])
+def test_device_factors_through_lse_and_prefix_entry_points(flags):
+    """attn_fwd_lse and attn_fwd_prefix with ATTN_FLAG_DESCALE_DEVICE (alone
+    and with each ablation flag): out and lse bit-identical to the calls with
+    the same factors passed from the host. The six floats sit at a 4-byte
+    offset inside a larger buffer (only 4-byte alignment is required)."""
+    import fp8_bf16_causal_amd._lib as L
+    q, k, v, scale = _bf16_inputs(63, S=700)
+    big = torch.full((16,), -1.0, dtype=torch.float32, device="cuda")
+    buf = big[1:7]
+    q8, k8, v8, _ = _chain(q, k, v, scale, buf)
+    torch.cuda.synchronize()
+    host = [float(x) for x in buf.cpu()[0::2]]
+    B, S, Hq, D = q8.shape
+    Hkv = k8.shape[2]
+    dev_flags = flags | L.ATTN_FLAG_DESCALE_DEVICE
+    for Sq in (S, 300):
+        qq = q8[:, S - Sq:].contiguous()
+        res = []
+        for fl, ds in ((dev_flags, buf.data_ptr()), (flags, host)):
+            out = torch.full((B, Sq, Hq, D), float("nan"), dtype=torch.bfloat16, device="cuda")
+            lse = torch.full((B, Hq, Sq), float("nan"), dtype=torch.float32, device="cuda")
+            if Sq == S:
+                rc = L.attn_fwd_lse(qq.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), lse.data_ptr(), B, Hq,
+                                    Hkv, S, D, D, 1, scale, L.ATTN_FP8_E4M3, ds, None, fl)
+            else:
+                rc = L.attn_fwd_prefix(qq.data_ptr(), k8.data_ptr(), v8.data_ptr(), out.data_ptr(), lse.data_ptr(), B,
+                                       Hq, Hkv, Sq, S, D, D, 1, scale, L.ATTN_FP8_E4M3, ds, None, fl)
+            assert rc == 0, L.attn_strerror(rc)
+            res.append((out, lse))
+        torch.cuda.synchronize()
+        (od, ld), (oh, lh) = res
+        same = torch.equal(od.view(torch.int16), oh.view(torch.int16)) and torch.equal(ld, lh)
+        _say(f"flags={flags} Sq={Sq} Sk={S}: device factors identical to host factors {same}")
+        assert same
+        assert not torch.isnan(ld).any()
