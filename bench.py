@@ -45,9 +45,9 @@ OTHER_CONFIGS = ["fp8_mla_s32k", "fp8_gqa_s16k_peaked"]
 
 # Sources whose text defines each kernel's code and launch: a stored HBM
 # traffic figure is used only while their hash matches the one recorded with it.
-_COMMON_SOURCES = ["fp8_bf16_causal_amd/csrc/attn_params.h", "fp8_bf16_causal_amd/csrc/attn_common.h",
-                   "fp8_bf16_causal_amd/csrc/attn_launch.h", "fp8_bf16_causal_amd/csrc/attn_api.cpp",
-                   "fp8_bf16_causal_amd/build.py"]
+_COMMON_SOURCES = ["include/fp8_bf16_causal.h", "fp8_bf16_causal_amd/csrc/attn_params.h",
+                   "fp8_bf16_causal_amd/csrc/attn_common.h", "fp8_bf16_causal_amd/csrc/attn_launch.h",
+                   "fp8_bf16_causal_amd/csrc/attn_api.cpp", "fp8_bf16_causal_amd/build.py"]
 KERNEL_SOURCES = {
     "fp8": _COMMON_SOURCES + ["fp8_bf16_causal_amd/csrc/attn_fwd_fp8.hip"],
     "bf16": _COMMON_SOURCES + ["fp8_bf16_causal_amd/csrc/attn_fwd_bf16.hip"],

@@ -126,7 +126,9 @@ int attn_fwd(const void* q, const void* k, const void* v, void* out, int B, int 
  *   descale_qkv  host pointer to {dq, dk, dv}, or NULL for {1, 1, 1}; read
  *                during the call only (with ATTN_FLAG_DESCALE_DEVICE: a device
  *                pointer to six floats, read by the kernels, see above)
- *   stream       a hipStream_t, or NULL for the null stream
+ *   stream       a hipStream_t created on the current device (the device the
+ *                pointers belong to and whose architecture is checked), or
+ *                NULL for that device's null stream
  *   flags        0, or ATTN_FLAG_* bits (FP8 only): ablations of the FP8
  *                softmax, device-resident dequantisation factors
  */
@@ -201,7 +203,8 @@ int attn_fwd_prefix(const void* q, const void* k, const void* v, void* out, floa
  *   rows      >= 1
  *   dim       64, 128, 192 or 256
  *   hadamard  0 or 1
- *   stream    a hipStream_t, or NULL for the null stream
+ *   stream    a hipStream_t of the current device, or NULL for its null
+ *             stream
  * Errors: ATTN_ERR_INVALID for a null or misaligned pointer, rows <= 0 or a
  * hadamard flag other than 0/1; ATTN_ERR_UNSUPPORTED for another dim or a
  * device that is not gfx950; ATTN_ERR_LAUNCH for a HIP error. Asynchronous
