@@ -207,12 +207,14 @@ def time_tp_shares(full_paths, steps=20, warmup=20):
         out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
         dq, dk, dv = inp.descale
         for _ in range(warmup):
-            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                                descale_q=dq, descale_k=dk, descale_v=dv, out=out)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in ev:
             a.record()
-            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                                descale_q=dq, descale_k=dk, descale_v=dv, out=out)
             b.record()
         torch.cuda.synchronize()
         ms = sorted(a.elapsed_time(b) for a, b in ev)[steps // 2]
@@ -247,12 +249,14 @@ def time_other_configs(steps=20, warmup=20):
         out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
         dq, dk, dv = inp.descale
         for _ in range(warmup):
-            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                                descale_q=dq, descale_k=dk, descale_v=dv, out=out)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for a, b in ev:
             a.record()
-            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                                descale_q=dq, descale_k=dk, descale_v=dv, out=out)
             b.record()
         torch.cuda.synchronize()
         ms = sorted(a.elapsed_time(b) for a, b in ev)[steps // 2]
@@ -443,7 +447,8 @@ def energy_study(seconds):
         dq, dk, dv = inp.descale
 
         def launch():
-            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                                descale_q=dq, descale_k=dk, descale_v=dv, out=out)
 
         launch()
         torch.cuda.synchronize()
@@ -576,7 +581,8 @@ def main():
         i = inputs[n]
         dq, dk, dv = i.descale
         ab = dict(exact_p=bool(args.fp8_flags & 1), block_scale=not (args.fp8_flags & 2)) if i.dtype == "fp8" else {}
-        fbc.flash_attn_func(i.q, i.k, i.v, i.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n], **ab)
+        fbc.flash_attn_func(i.q, i.k, i.v, i.scale, causal=True,
+                            descale_q=dq, descale_k=dk, descale_v=dv, out=outs[n], **ab)
 
     # everything the timed region needs is set up before the settle and warmup
     # launches, so that the GPU does not idle (and boost its clock) in front

@@ -30,8 +30,23 @@ def _raise(code: int):
     raise RuntimeError(msg)
 
 
-def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, descale_k=None, descale_v=None,
-                    out=None, exact_p=False, block_scale=True, return_lse=False, descale_device=None):
+def _factor(x, name):
+    """A per-tensor dequantisation factor: a number, or a one-element tensor
+    (flash-attention's per-(batch, head) descale tensors are accepted only when
+    they hold a single value)."""
+    if x is None or isinstance(x, (int, float)):
+        return x
+    if hasattr(x, "numel"):
+        if x.numel() != 1:
+            raise ValueError(f"{name}: one factor per tensor (a number or a one-element tensor)")
+        return float(x.reshape(-1)[0])
+    return float(x)
+
+
+def flash_attn_func(q, k, v, softmax_scale=None, causal=False, *, q_descale=None, k_descale=None, v_descale=None,
+                    window_size=(-1, -1), softcap=0.0, alibi_slopes=None, deterministic=False, dropout_p=0.0,
+                    descale_q=None, descale_k=None, descale_v=None, out=None, exact_p=False, block_scale=True,
+                    return_lse=False, descale_device=None):
     """Causal prefill attention on torch tensors in (batch, seq, heads, dim)
     layout: bfloat16, or float8_e4m3fn with optional per-tensor dequantisation
     factors (ValueError for a factor other than 1 with bfloat16). Returns a
@@ -45,7 +60,31 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=True, descale_q=None, de
     contiguous float32 tensor on q's device holding {dq, amax_q, dk, amax_k,
     dv, amax_v} (three quantize_e4m3 calls with scale_out=buf[0:2], buf[2:4],
     buf[4:6]), read by the kernels: no host round trip
-    (ATTN_FLAG_DESCALE_DEVICE)."""
+    (ATTN_FLAG_DESCALE_DEVICE).
+
+    The positional order (q, k, v, softmax_scale, causal) and the keywords
+    q_descale / k_descale / v_descale, window_size, softcap, alibi_slopes,
+    deterministic and dropout_p follow flash-attention's FP8-capable
+    flash_attn_func, so existing calls keep their meaning: causal defaults to
+    False there, and a non-causal call raises NotImplementedError here rather
+    than silently computing causal attention; so do a sliding window, a
+    softcap, ALiBi slopes and dropout. q_descale etc. are aliases of
+    descale_q etc. (one factor per tensor). The kernels are deterministic
+    whatever `deterministic` says."""
+    if dropout_p != 0.0:
+        raise NotImplementedError("dropout is not supported (inference prefill forward only)")
+    if softcap != 0.0 or alibi_slopes is not None:
+        raise NotImplementedError("softcap and ALiBi slopes are not supported")
+    if tuple(window_size) not in ((-1, -1), (-1, 0)) or (tuple(window_size) == (-1, 0) and not causal):
+        raise NotImplementedError("sliding-window attention is not supported (window_size must be (-1, -1))")
+    if not causal:
+        raise NotImplementedError("only causal attention is implemented (pass causal=True)")
+    for a, b, name in ((q_descale, descale_q, "q"), (k_descale, descale_k, "k"), (v_descale, descale_v, "v")):
+        if a is not None and b is not None:
+            raise ValueError(f"give {name}_descale or descale_{name}, not both")
+    descale_q = _factor(descale_q if q_descale is None else q_descale, "q_descale")
+    descale_k = _factor(descale_k if k_descale is None else k_descale, "k_descale")
+    descale_v = _factor(descale_v if v_descale is None else v_descale, "v_descale")
     import torch
 
     if q.dtype == torch.bfloat16:

@@ -85,7 +85,7 @@ def test_binding_has_no_cpu_path():
     import torch
     q = torch.zeros(1, 4, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
-        fbc.flash_attn_func(q, q, q)
+        fbc.flash_attn_func(q, q, q, causal=True)
 
 
 @pytest.mark.parametrize("args,code", [
@@ -133,4 +133,35 @@ def test_flash_attn_func_refuses_descales_with_bf16():
     q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
     for kw in (dict(descale_q=0.5), dict(descale_k=2.0), dict(descale_v=0.25)):
         with pytest.raises(ValueError, match="descale"):
-            fbc.flash_attn_func(q, q, q, **kw)
+            fbc.flash_attn_func(q, q, q, causal=True, **kw)
+
+
+def test_flash_attn_func_keeps_flash_attention_call_meanings():
+    """flash_attn_func takes flash-attention's positional order (q, k, v,
+    softmax_scale, causal) and keywords; what the kernels do not implement is
+    refused before any device work instead of being computed differently:
+    causal=False (flash-attention's default), dropout, a sliding window,
+    softcap, ALiBi. q_descale/k_descale/v_descale are aliases of
+    descale_q/k/v, one factor per tensor."""
+    import torch
+
+    q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
+    with pytest.raises(NotImplementedError, match="causal"):
+        fbc.flash_attn_func(q, q, q)
+    with pytest.raises(NotImplementedError, match="causal"):
+        fbc.flash_attn_func(q, q, q, None, False)
+    for kw in (dict(dropout_p=0.1), dict(window_size=(128, 0)), dict(window_size=(-1, 64)), dict(softcap=30.0),
+               dict(alibi_slopes=torch.zeros(2))):
+        with pytest.raises(NotImplementedError):
+            fbc.flash_attn_func(q, q, q, causal=True, **kw)
+    with pytest.raises(ValueError, match="not both"):
+        fbc.flash_attn_func(q, q, q, causal=True, q_descale=1.0, descale_q=1.0)
+    with pytest.raises(ValueError, match="one factor per tensor"):
+        fbc.flash_attn_func(q, q, q, causal=True, k_descale=torch.ones(1, 2))
+    with pytest.raises(ValueError, match="descale"):  # bfloat16 with a factor, through the alias
+        fbc.flash_attn_func(q, q, q, causal=True, v_descale=torch.full((1,), 0.5))
+    # accepted options reach the device checks (CPU tensors: refused there, no fallback)
+    for kw in (dict(window_size=(-1, -1)), dict(window_size=(-1, 0)), dict(deterministic=True),
+               dict(q_descale=torch.ones(1))):
+        with pytest.raises(ValueError, match="one GPU"):
+            fbc.flash_attn_func(q, q, q, 0.1, True, **kw)

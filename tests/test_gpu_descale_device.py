@@ -45,7 +45,7 @@ def _chain(q, k, v, scale, buf):
     q8, _ = fbc.quantize_e4m3(q, hadamard=True, scale_out=buf[0:2])
     k8, _ = fbc.quantize_e4m3(k, hadamard=True, scale_out=buf[2:4])
     v8, _ = fbc.quantize_e4m3(v, hadamard=False, scale_out=buf[4:6])
-    out = fbc.flash_attn_func(q8, k8, v8, scale, descale_device=buf)
+    out = fbc.flash_attn_func(q8, k8, v8, scale, causal=True, descale_device=buf)
     return q8, k8, v8, out
 
 
@@ -56,7 +56,7 @@ def test_device_factors_equal_host_factors_and_meet_the_bar():
     q8, k8, v8, out_dev = _chain(q, k, v, scale, buf)
     torch.cuda.synchronize()
     dq, _, dk, _, dv, _ = [float(x) for x in buf.cpu()]
-    out_host = fbc.flash_attn_func(q8, k8, v8, scale, descale_q=dq, descale_k=dk, descale_v=dv)
+    out_host = fbc.flash_attn_func(q8, k8, v8, scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv)
     torch.cuda.synchronize()
     assert torch.equal(out_dev.view(torch.int16), out_host.view(torch.int16))
     ref = oracle.attention(synth.raw_codes(q8), synth.raw_codes(k8), synth.raw_codes(v8), oracle.FP8_E4M3, scale,

@@ -73,7 +73,7 @@ def test_graph_replays_reproduce_eager_results():
     for r in range(4):
         # the program's own eager work between replays: a library call on other
         # inputs and a torch product, then the outputs overwritten
-        fbc.flash_attn_func(other.q, other.k, other.v, other.scale, descale_q=other.descale[0],
+        fbc.flash_attn_func(other.q, other.k, other.v, other.scale, causal=True, descale_q=other.descale[0],
                             descale_k=other.descale[1], descale_v=other.descale[2])
         torch.mm(x[:1024].float(), x[:1024].float().t())
         for t in (o8, o16):

@@ -95,7 +95,7 @@ def _run(q, k, v, scale):
     import fp8_bf16_causal_amd as fbc
     dev = torch.device("cuda", 0)
     t = [torch.from_numpy(x).to(dev).view(torch.float8_e4m3fn) for x in (q, k, v)]
-    o = fbc.flash_attn_func(*t, softmax_scale=scale)
+    o = fbc.flash_attn_func(*t, softmax_scale=scale, causal=True)
     torch.cuda.synchronize()
     return o.float().cpu().numpy()[0]  # [S, H, 128]
 

@@ -46,8 +46,9 @@ def _run(inp, exact_p=False):
     dev = torch.device("cuda", 0)
     q, k, v = (t if t.is_cuda else t.to(dev) for t in (inp.q, inp.k, inp.v))
     ab = dict(exact_p=exact_p) if inp.dtype == "fp8" else {}
-    o1 = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, **ab)
-    o2, lse = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, return_lse=True,
+    o1 = fbc.flash_attn_func(q, k, v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv, **ab)
+    o2, lse = fbc.flash_attn_func(q, k, v, inp.scale, causal=True,
+                                  descale_q=dq, descale_k=dk, descale_v=dv, return_lse=True,
                                   **ab)
     torch.cuda.synchronize()
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "O changed with the lse output"

@@ -45,10 +45,10 @@ def run_gpu(inp, out=None, stream=None):
     q, k, v = (t if t.is_cuda else t.to(dev) for t in (inp.q, inp.k, inp.v))
     if stream is not None:
         with torch.cuda.stream(stream):
-            o = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+            o = fbc.flash_attn_func(q, k, v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
         stream.synchronize()
     else:
-        o = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+        o = fbc.flash_attn_func(q, k, v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
         torch.cuda.synchronize()
     return o
 
@@ -245,7 +245,8 @@ def test_fp8_ablations_follow_the_model(exact_p, block_scale):
     inp = synth.make_inputs(B=1, S=700, Hq=2, Hkv=1, Dqk=128, Dv=128, dtype="fp8", seed=41)
     dq, dk, dv = inp.descale
     dev = torch.device("cuda", 0)
-    out = fbc.flash_attn_func(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.scale, descale_q=dq, descale_k=dk,
+    out = fbc.flash_attn_func(inp.q.to(dev), inp.k.to(dev), inp.v.to(dev), inp.scale, causal=True,
+                              descale_q=dq, descale_k=dk,
                               descale_v=dv, exact_p=exact_p, block_scale=block_scale)
     torch.cuda.synchronize()
     out = out.float().cpu().numpy().astype(np.float64)
@@ -267,7 +268,7 @@ def test_fp8_exact_p_meets_the_bar_and_beats_lean_p():
     ref = oracle_out(inp)
     errs = {}
     for ex in (False, True):
-        o = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, exact_p=ex)
+        o = fbc.flash_attn_func(q, k, v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv, exact_p=ex)
         torch.cuda.synchronize()
         got = o.float().cpu().numpy()
         errs[ex] = check(inp, got, ref, f"fp8 exact_p={ex}")[0]
@@ -291,7 +292,8 @@ def test_fp8_block_scaling_matters_on_peaked_inputs():
     lim = vmax(inp)
     rr, ma = {}, {}
     for bs in (True, False):
-        o = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, block_scale=bs)
+        o = fbc.flash_attn_func(q, k, v, inp.scale, causal=True,
+                                descale_q=dq, descale_k=dk, descale_v=dv, block_scale=bs)
         torch.cuda.synchronize()
         got = np.stack([o[b, i, h].float().cpu().numpy() for (b, h, i) in rows]).astype(np.float64)
         rr[bs], ma[bs] = _rel(got, ref), float(np.max(np.abs(got - ref))) / lim
@@ -335,10 +337,11 @@ def test_bitwise_deterministic_full_size(name):
     dq, dk, dv = inp.descale
     out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
     _say(f"case determinism {name} x100")
-    fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+    fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
     first = out.clone()
     for _ in range(99):
-        fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, out=out)
+        fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                            descale_q=dq, descale_k=dk, descale_v=dv, out=out)
         assert torch.equal(out.view(torch.int16), first.view(torch.int16))
     torch.cuda.synchronize()
 
@@ -372,7 +375,8 @@ def test_concurrent_calls_from_host_threads_on_separate_streams():
         dq, dk, dv = inp.descale
         s = torch.cuda.Stream()
         with torch.cuda.stream(s):
-            outs = [fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv)
+            outs = [fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True,
+                                        descale_q=dq, descale_k=dk, descale_v=dv)
                     for _ in range(20)]
         s.synchronize()
         for o in outs:

@@ -44,7 +44,8 @@ def _gpu(inp):
     import fp8_bf16_causal_amd as fbc
     dq, dk, dv = inp.descale
     q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
-    out, lse = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv, return_lse=True)
+    out, lse = fbc.flash_attn_func(q, k, v, inp.scale, causal=True,
+                                   descale_q=dq, descale_k=dk, descale_v=dv, return_lse=True)
     torch.cuda.synchronize()
     return out, lse
 
@@ -99,7 +100,7 @@ def test_prefix_with_equal_lengths_is_the_plain_call(dtype):
     inp = synth.make_inputs(B=1, S=700, Hq=4, Hkv=2, Dqk=128, Dv=128, dtype=dtype, seed=5)
     q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
     dq, dk, dv = inp.descale
-    a = fbc.flash_attn_func(q, k, v, inp.scale, descale_q=dq, descale_k=dk, descale_v=dv)
+    a = fbc.flash_attn_func(q, k, v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv)
     b = torch.empty_like(a)
     rc = fbc.attn_fwd_prefix(q.data_ptr(), k.data_ptr(), v.data_ptr(), b.data_ptr(), None, 1, 4, 2, 700, 700, 128,
                              128, 1, inp.scale, fbc.ATTN_BF16 if dtype == "bf16" else fbc.ATTN_FP8_E4M3,

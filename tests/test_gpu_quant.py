@@ -112,7 +112,7 @@ def test_rotation_lowers_fp8_attention_error_on_peaked_inputs():
         ck, sk = fbc.quantize_e4m3(k, hadamard=rot)
         cv, sv = fbc.quantize_e4m3(v, hadamard=False)
         ds = [float(t[0]) for t in (sq, sk, sv)]
-        out = fbc.flash_attn_func(cq, ck, cv, inp.scale, descale_q=ds[0], descale_k=ds[1], descale_v=ds[2])
+        out = fbc.flash_attn_func(cq, ck, cv, inp.scale, causal=True, descale_q=ds[0], descale_k=ds[1], descale_v=ds[2])
         torch.cuda.synchronize()
         got = np.stack([out[b, i, h].float().cpu().numpy() for (b, h, i) in rows]).astype(np.float64)
         err[rot] = math.sqrt(float(np.sum((got - ref) ** 2)) / float(np.sum(ref ** 2)))
