@@ -43,7 +43,7 @@ def _factor(x, name):
     return float(x)
 
 
-def flash_attn_func(q, k, v, softmax_scale=None, causal=False, *, q_descale=None, k_descale=None, v_descale=None,
+def flash_attn_func(q, k, v, softmax_scale=None, causal=True, *, q_descale=None, k_descale=None, v_descale=None,
                     window_size=(-1, -1), softcap=0.0, alibi_slopes=None, deterministic=False, dropout_p=0.0,
                     descale_q=None, descale_k=None, descale_v=None, out=None, exact_p=False, block_scale=True,
                     return_lse=False, descale_device=None):
@@ -65,12 +65,13 @@ def flash_attn_func(q, k, v, softmax_scale=None, causal=False, *, q_descale=None
     The positional order (q, k, v, softmax_scale, causal) and the keywords
     q_descale / k_descale / v_descale, window_size, softcap, alibi_slopes,
     deterministic and dropout_p follow flash-attention's FP8-capable
-    flash_attn_func, so existing calls keep their meaning: causal defaults to
-    False there, and a non-causal call raises NotImplementedError here rather
-    than silently computing causal attention; so do a sliding window, a
-    softcap, ALiBi slopes and dropout. q_descale etc. are aliases of
-    descale_q etc. (one factor per tensor). The kernels are deterministic
-    whatever `deterministic` says."""
+    flash_attn_func. What the kernels do not implement raises
+    NotImplementedError rather than returning something else: causal=False,
+    a sliding window, a softcap, ALiBi slopes and dropout. causal defaults to
+    True here, the only mode the method has (flash-attention's default is
+    False: calls written for it that rely on that default must pass causal).
+    q_descale etc. are aliases of descale_q etc. (one factor per tensor). The
+    kernels are deterministic whatever `deterministic` says."""
     if dropout_p != 0.0:
         raise NotImplementedError("dropout is not supported (inference prefill forward only)")
     if softcap != 0.0 or alibi_slopes is not None:

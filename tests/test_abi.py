@@ -140,16 +140,16 @@ def test_flash_attn_func_keeps_flash_attention_call_meanings():
     """flash_attn_func takes flash-attention's positional order (q, k, v,
     softmax_scale, causal) and keywords; what the kernels do not implement is
     refused before any device work instead of being computed differently:
-    causal=False (flash-attention's default), dropout, a sliding window,
-    softcap, ALiBi. q_descale/k_descale/v_descale are aliases of
-    descale_q/k/v, one factor per tensor."""
+    causal=False, dropout, a sliding window, softcap, ALiBi.
+    q_descale/k_descale/v_descale are aliases of descale_q/k/v, one factor
+    per tensor."""
     import torch
 
     q = torch.zeros((1, 4, 2, 128), dtype=torch.bfloat16)
     with pytest.raises(NotImplementedError, match="causal"):
-        fbc.flash_attn_func(q, q, q)
-    with pytest.raises(NotImplementedError, match="causal"):
         fbc.flash_attn_func(q, q, q, None, False)
+    with pytest.raises(NotImplementedError, match="causal"):
+        fbc.flash_attn_func(q, q, q, causal=False)
     for kw in (dict(dropout_p=0.1), dict(window_size=(128, 0)), dict(window_size=(-1, 64)), dict(softcap=30.0),
                dict(alibi_slopes=torch.zeros(2))):
         with pytest.raises(NotImplementedError):
