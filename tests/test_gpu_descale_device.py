@@ -136,3 +136,24 @@ def test_device_factors_through_lse_and_prefix_entry_points(flags):
         _say(f"flags={flags} Sq={Sq} Sk={S}: device factors identical to host factors {same}")
         assert same
         assert not torch.isnan(ld).any()
+
+
+def test_flash_attention_keyword_aliases_give_the_same_result():
+    """flash_attn_func's flash-attention spellings (q_descale/k_descale/
+    v_descale as one-element device tensors, window_size=(-1, 0) with causal,
+    deterministic=True, positional softmax_scale and causal) give the same
+    bits as the library's own keywords."""
+    import fp8_bf16_causal_amd as fbc
+    q, k, v, scale = _bf16_inputs(64, S=500)
+    q8, sq = fbc.quantize_e4m3(q, hadamard=True)
+    k8, sk = fbc.quantize_e4m3(k, hadamard=True)
+    v8, sv = fbc.quantize_e4m3(v)
+    torch.cuda.synchronize()
+    dq, dk, dv = float(sq[0]), float(sk[0]), float(sv[0])
+    a = fbc.flash_attn_func(q8, k8, v8, scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv)
+    b = fbc.flash_attn_func(q8, k8, v8, scale, True, q_descale=sq[0:1], k_descale=sk[0:1], v_descale=sv[0:1],
+                            window_size=(-1, 0), deterministic=True)
+    torch.cuda.synchronize()
+    same = torch.equal(a.view(torch.int16), b.view(torch.int16))
+    _say(f"flash-attention keyword spellings identical {same}")
+    assert same
