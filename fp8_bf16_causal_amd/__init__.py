@@ -18,7 +18,7 @@ from ._lib import (ATTN_BF16, ATTN_ERR_INVALID, ATTN_ERR_LAUNCH, ATTN_ERR_UNSUPP
 __all__ = ["attn_fwd", "attn_fwd_ex", "attn_fwd_lse", "attn_fwd_prefix", "attn_quantize_e4m3", "attn_strerror",
            "flash_attn_func", "quantize_e4m3", "ATTN_BF16", "ATTN_FP8_E4M3", "ATTN_OK", "ATTN_ERR_INVALID",
            "ATTN_ERR_UNSUPPORTED", "ATTN_ERR_LAUNCH", "ATTN_FLAG_EXACT_P", "ATTN_FLAG_NO_BLOCKSCALE",
-           "ATTN_FLAG_DESCALE_DEVICE"]
+           "ATTN_FLAG_DESCALE_DEVICE", "flash_attn_fp8_func"]
 
 
 def _raise(code: int):
@@ -175,3 +175,25 @@ def quantize_e4m3(x, hadamard=False, scale_out=None):
     if rc != ATTN_OK:
         _raise(rc)
     return y, scale
+
+
+def flash_attn_fp8_func(q, k, v, softmax_scale=None, causal=True, hadamard=True, out=None, return_lse=False,
+                        exact_p=False, block_scale=True):
+    """FP8 prefill from bfloat16 tensors in one call: Q and K quantised to
+    e4m3fn with the Hadamard rotation (hadamard=True, the default; one
+    orthogonal rotation on both leaves Q K^T unchanged) and V without, each
+    with its own per-tensor factor, then the FP8 attention reading those
+    factors on the device (ATTN_FLAG_DESCALE_DEVICE): four launches on the
+    current stream, no host synchronisation. Returns what flash_attn_func
+    returns. The codes and factors are temporaries of this call; use
+    quantize_e4m3 and flash_attn_func(descale_device=...) to keep them."""
+    import torch
+
+    if q.dtype != torch.bfloat16 or k.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("flash_attn_fp8_func takes bfloat16 q, k and v")
+    buf = torch.empty(6, dtype=torch.float32, device=q.device)
+    q8, _ = quantize_e4m3(q, hadamard=hadamard, scale_out=buf[0:2])
+    k8, _ = quantize_e4m3(k, hadamard=hadamard, scale_out=buf[2:4])
+    v8, _ = quantize_e4m3(v, hadamard=False, scale_out=buf[4:6])
+    return flash_attn_func(q8, k8, v8, softmax_scale, causal, out=out, return_lse=return_lse, exact_p=exact_p,
+                           block_scale=block_scale, descale_device=buf)

@@ -165,3 +165,11 @@ def test_flash_attn_func_keeps_flash_attention_call_meanings():
                dict(q_descale=torch.ones(1))):
         with pytest.raises(ValueError, match="one GPU"):
             fbc.flash_attn_func(q, q, q, 0.1, True, **kw)
+
+
+def test_flash_attn_fp8_func_takes_bfloat16_only():
+    import torch
+
+    q = torch.zeros((1, 4, 2, 128), dtype=torch.float32)
+    with pytest.raises(TypeError, match="bfloat16"):
+        fbc.flash_attn_fp8_func(q, q, q)

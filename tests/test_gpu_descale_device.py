@@ -157,3 +157,22 @@ def test_flash_attention_keyword_aliases_give_the_same_result():
     same = torch.equal(a.view(torch.int16), b.view(torch.int16))
     _say(f"flash-attention keyword spellings identical {same}")
     assert same
+
+
+@pytest.mark.parametrize("hadamard", [True, False])
+def test_one_call_fp8_prefill_from_bf16(hadamard):
+    """flash_attn_fp8_func: the same bits as the chain of three quantize calls
+    and the attention on device factors, with and without the rotation (and
+    with return_lse, the same lse as the chain's)."""
+    import fp8_bf16_causal_amd as fbc
+    q, k, v, scale = _bf16_inputs(65, S=600)
+    buf = torch.empty(6, dtype=torch.float32, device="cuda")
+    q8, _ = fbc.quantize_e4m3(q, hadamard=hadamard, scale_out=buf[0:2])
+    k8, _ = fbc.quantize_e4m3(k, hadamard=hadamard, scale_out=buf[2:4])
+    v8, _ = fbc.quantize_e4m3(v, scale_out=buf[4:6])
+    ref, ref_lse = fbc.flash_attn_func(q8, k8, v8, scale, causal=True, descale_device=buf, return_lse=True)
+    got, got_lse = fbc.flash_attn_fp8_func(q, k, v, scale, hadamard=hadamard, return_lse=True)
+    torch.cuda.synchronize()
+    same = torch.equal(got.view(torch.int16), ref.view(torch.int16)) and torch.equal(got_lse, ref_lse)
+    _say(f"one-call FP8 prefill (hadamard={hadamard}) identical to the chain {same}")
+    assert same
