@@ -150,6 +150,40 @@ def time_quant_prologue(steps, warmup):
     return res
 
 
+
+def time_fp8_from_bf16(inp, steps=20, warmup=10):
+    """FP8 prefill from BF16 activations end to end, on the BF16 benchmark's
+    inputs (1 x 32K x 32 x 128): flash_attn_fp8_func, i.e. three quantize
+    calls (Q and K with the Hadamard rotation) and the FP8 attention on the
+    factors they leave on the device, against the BF16 attention on the same
+    tensors. The two are timed alternately, median of `steps` each."""
+    import torch
+
+    import fp8_bf16_causal_amd as fbc
+
+    p = inp.shape
+    out = torch.empty((p["B"], p["S"], p["Hq"], p["Dv"]), dtype=torch.bfloat16, device="cuda")
+    runs = {"fp8_chain": lambda: fbc.flash_attn_fp8_func(inp.q, inp.k, inp.v, inp.scale, out=out),
+            "bf16": lambda: fbc.flash_attn_func(inp.q, inp.k, inp.v, inp.scale, causal=True, out=out)}
+    for _ in range(warmup):
+        for f in runs.values():
+            f()
+    torch.cuda.synchronize()
+    ev = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+          for k in runs}
+    for s in range(steps):
+        for k, f in runs.items():
+            ev[k][s][0].record()
+            f()
+            ev[k][s][1].record()
+    torch.cuda.synchronize()
+    med = {k: sorted(a.elapsed_time(b) for a, b in v)[steps // 2] for k, v in ev.items()}
+    del out
+    return {"workload": "bf16_mha_s32k tensors; FP8 path = quantize Q, K (rotated) and V, then FP8 attention "
+                        "on device factors (flash_attn_fp8_func)",
+            "fp8_chain_ms_median": round(med["fp8_chain"], 4), "bf16_attention_ms_median": round(med["bf16"], 4),
+            "speedup_vs_bf16": round(med["bf16"] / med["fp8_chain"], 3)}
+
 # One GPU's share of each workload under 8-way tensor parallelism over heads
 # (each GPU takes 1/8 of the KV heads with their query heads; no exchange).
 TP_SHARES = [("fp8_mha_s32k", dict(Hq=4, Hkv=4)), ("bf16_mha_s32k", dict(Hq=4, Hkv=4)),
@@ -677,6 +711,8 @@ def main():
         line["tp8_shares"] = time_tp_shares({**paths, **line.get("other_configs", {})})
     if not args.no_quant and not args.fp8_flags:
         line["quantize_prologue"] = time_quant_prologue(50, 10)
+        if "bf16_mha_s32k" in inputs:
+            line["fp8_from_bf16"] = time_fp8_from_bf16(inputs["bf16_mha_s32k"])
     if not args.no_cpu_baseline:
         threads = min(int(os.environ.get("OMP_NUM_THREADS", "16")), os.cpu_count() or 1, 16)
         line["cpu_baseline"] = cpu_baseline(inputs, args.cpu_rows, threads)
