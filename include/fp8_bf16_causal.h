@@ -146,9 +146,11 @@ int attn_fwd_ex(const void* q, const void* k, const void* v, void* out, int B, i
  *   lse[(b*Hq + h)*S + i] = ln sum_{j<=i} exp(scale*dq*dk*<q_i, k_j>)
  *                        ~= ln(2) * (m c + log2 l),  c = scale*dq*dk*log2(e),
  * where l sums the probabilities the P V product applies: BF16-rounded (within
- * about 0.004 of the exact value), or, for FP8, the Lean P codes with their
- * block scales (within ln(1.075) ~ 0.072: the encoding's largest relative
- * error).
+ * ln(1 + 2^-8) ~ 0.0039 of the exact value: BF16 keeps 8 significant bits),
+ * or, for FP8, the Lean P codes with their block scales (within about 0.080:
+ * a code in e4m3's normal range decodes to 0.927-1.073 times its probability,
+ * and keys more than about 13 binades below their block's maximum add at
+ * most 0.0043 of the sum).
  *   lse   device pointer to B*Hq*S floats (4-byte aligned), written entirely;
  *         float32, natural log, layout [B][Hq][S]
  * Other arguments and errors as attn_fwd_ex; a null or misaligned lse is

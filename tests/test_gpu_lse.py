@@ -2,13 +2,21 @@
 ABI) against the fp64 oracle's lse_i = ln sum_{j<=i} exp(z_ij).
 
 Tolerances, from the arithmetic: the kernels report ln2 * (m c + log2 l) with
-l the sum of the probabilities the P V product applies.
-  BF16: each probability is rounded to BF16 (relative error <= 2^-9), so l is
-        within a factor 1 +- 2^-9 of the exact sum: |d lse| <= ln(1 + 2^-9)
-        ~= 0.002, plus fp32 rounding of m c and log2 -> bound 3e-3.
-  FP8:  each Lean P code decodes within 7.5% of its probability (the pages'
-        bound), so |d lse| <= ln(1.075) ~= 0.0723 -> bound 0.075 (exact-P
-        ablation: 1/17 -> ln(18/17) ~= 0.0572 -> 0.06).
+l the sum of the probabilities the P V product applies, so the error is the
+log of the ratio of that sum to the exact one.
+  BF16: each probability is rounded to nearest BF16 (8 significant bits), so
+        it is within a factor (1 + 2^-8)^(+-1) of its value and
+        |d lse| <= ln(1 + 2^-8) ~= 0.0039; fp32 rounding of m c and the
+        log2 adds far less -> bar 4e-3.
+  FP8:  a Lean P code in e4m3's normal range decodes to 0.9273-1.0727 times
+        its probability (tests/test_leanp_model.py); a key whose block-scaled
+        probability is below 2^-6 is off by < 0.0085, and each 64-key block's
+        scaled maximum is at least 2^7, so such keys move the sum by at most
+        64 * 0.0085 / 128 ~= 0.0043 of it: |d lse| <= -ln(0.9273 - 0.0043)
+        ~= 0.080 (the larger side) -> bar 0.081. Exact-P ablation: e4m3
+        rounding within a factor 17/16 in the normal range, half a 2^-9 step
+        (2^-11 of a block's scaled maximum) below it:
+        |d lse| <= -ln(16/17 - 2^-11) ~= 0.061 -> bar 0.062.
 The output O must be bitwise the same as without the extra result.
 """
 import math
@@ -23,7 +31,8 @@ from fp8_bf16_causal_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-LSE_TOL = {"bf16": 3e-3, "fp8": 0.075}
+LSE_TOL = {"bf16": 4e-3, "fp8": 0.081}
+LSE_TOL_EXACT_P = 0.062
 
 
 def _say(msg):
@@ -88,7 +97,7 @@ def test_lse_fp8_peaked_and_exact_p():
     _, lse = _run(inp)
     _check(lse.cpu().numpy(), ref, LSE_TOL["fp8"], "fp8 peaked lean P")
     _, lse = _run(inp, exact_p=True)
-    _check(lse.cpu().numpy(), ref, 0.06, "fp8 peaked exact P")
+    _check(lse.cpu().numpy(), ref, LSE_TOL_EXACT_P, "fp8 peaked exact P")
 
 
 @pytest.mark.parametrize("name", ["fp8_mha_s32k", "bf16_mha_s32k"])

@@ -41,6 +41,24 @@ def test_leanp_error_bound_and_constant(golden):
     assert _rel_err_leanp(55.55).max() > bound and _rel_err_leanp(55.70).max() > bound
 
 
+def test_leanp_ratio_range_and_subnormal_error():
+    """The two facts the log-sum-exp bound of the FP8 path rests on: over the
+    e4m3 normal range a Lean P code decodes to between 0.9273 and 1.0727 times
+    its probability (so |ln ratio| <= 0.0755), and below it (probabilities
+    under 2^-6 after block scaling, subnormal or zero codes) it is off by less
+    than 0.0085 in absolute terms."""
+    x = np.linspace(-6.0, 8.0, 400001)
+    r = leanp.e4m3_value(leanp.leanp_code(x)) / 2.0 ** x
+    assert 0.9273 <= r.min() and r.max() <= 1.0727
+    assert max(-np.log(r.min()), np.log(r.max())) <= 0.0755
+    xs = np.linspace(-40.0, -6.0, 400001)[:-1]
+    d = np.abs(leanp.e4m3_value(leanp.leanp_code(xs)) - 2.0 ** xs)
+    assert d.max() < 0.0085
+    # exact rounding: at most half a subnormal step, 2^-10
+    de = np.abs(leanp.e4m3_value(leanp.e4m3_round_rne(2.0 ** xs)) - 2.0 ** xs)
+    assert de.max() <= 2.0 ** -10
+
+
 def test_code_grows_by_eight_per_doubling(golden):
     step = golden["fp8_e4m3_code_step_per_doubling"]["value"]
     x = np.linspace(-5.0, 6.9, 1191)
