@@ -3,7 +3,8 @@ Sq queries, the last Sq positions of Sk >= Sq keys, query i seeing keys
 j <= i + Sk - Sq. Compared element by element with the fp64 oracle at the
 path's bars (BF16: relative RMS <= 1e-2, max |err| <= 3e-2; FP8: relative
 RMS <= 4e-2, max |err| <= 0.1 max|V dv|), and the log-sum-exp at the bounds
-derived for attn_fwd_lse (BF16 4e-3, FP8 0.081; tests/test_gpu_lse.py)."""
+derived for attn_fwd_lse (tests/test_gpu_lse.py: BF16 4e-3; FP8 0.095 plus the
+per-row bound of the matrix instruction's score truncation)."""
 import math
 import sys
 
@@ -13,11 +14,11 @@ import torch
 
 import oracle
 from fp8_bf16_causal_amd import synth
+from test_gpu_lse import lse_tol
 
 pytestmark = pytest.mark.gpu
 
 TOL = {"bf16": (1e-2, 3e-2), "fp8": (4e-2, 0.1)}
-LSE_TOL = {"bf16": 4e-3, "fp8": 0.081}
 
 
 def _say(msg):
@@ -62,7 +63,9 @@ def _vmax(inp):
     return float(np.max(np.abs(oracle.dequantize(synth.raw_codes(inp.v), dt, inp.descale[2]))))
 
 
-def _check(inp, got, ref, got_lse, ref_lse, label):
+def _check(inp, got, ref, got_lse, ref_lse, label, rows=None):
+    """Output at the parity bars; lse per row at lse_tol (rows: the sampled
+    (b, h, i) the lse values belong to, else the whole [B, Hq, Sq])."""
     got = got.astype(np.float64)
     assert np.all(np.isfinite(got)), label
     err = got - ref
@@ -71,10 +74,15 @@ def _check(inp, got, ref, got_lse, ref_lse, label):
     lim_rr, lim_ma = TOL[inp.dtype]
     if inp.dtype == "fp8":
         lim_ma *= _vmax(inp)
-    le = float(np.max(np.abs(np.asarray(got_lse, dtype=np.float64) - ref_lse)))
-    _say(f"{label}: rel_rms={rr:.3e} maxabs={ma:.3e} lse max err={le:.3e}")
+    tol = lse_tol(inp)
+    if rows is not None:
+        tol = np.array([tol[b, h, i] for b, h, i in rows])
+    le = np.abs(np.asarray(got_lse, dtype=np.float64) - ref_lse)
+    worst = int(np.argmax(le - tol))
+    _say(f"{label}: rel_rms={rr:.3e} maxabs={ma:.3e} lse max err={le.max():.3e} "
+         f"(tightest row {le.flat[worst]:.3e} <= {tol.flat[worst]:.3e})")
     assert rr <= lim_rr and ma <= lim_ma, label
-    assert le <= LSE_TOL[inp.dtype], label
+    assert np.all(le <= tol), label
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
@@ -131,7 +139,8 @@ def test_prefix_long_context_chunk_sampled_rows(dtype):
     ref, ref_lse = _oracle(inp, rows=rows)
     got = np.stack([out[b, i, h].float().cpu().numpy() for b, h, i in rows])
     l = lse.cpu().numpy()
-    _check(inp, got, ref, np.array([l[b, h, i] for b, h, i in rows]), ref_lse, f"{dtype} chunk sampled rows")
+    _check(inp, got, ref, np.array([l[b, h, i] for b, h, i in rows]), ref_lse, f"{dtype} chunk sampled rows",
+           rows=rows)
 
 
 @pytest.mark.parametrize("case", range(24))

@@ -2,14 +2,17 @@
 head dims, dtype, input structure and softmax scale drawn together, each case
 compared over its whole output with the fp64 oracle at the parity bars
 (BF16: relative RMS <= 1e-2, max abs <= 3e-2; FP8: relative RMS <= 4e-2,
-max abs <= 0.1 max|V dv|). The draws are fixed by the case index, so a
+max abs <= 0.1 max|V dv|), and its per-row log-sum-exp at the bounds derived
+in tests/test_gpu_lse.py. The draws are fixed by the case index, so a
 failure names a reproducible configuration."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from fp8_bf16_causal_amd import synth
-from test_gpu_parity import full_check
+from test_gpu_lse import lse_tol
+from test_gpu_parity import _say, check
 
 pytestmark = pytest.mark.gpu
 
@@ -35,7 +38,23 @@ def draw(case):
 
 @pytest.mark.parametrize("case", range(N_CASES))
 def test_random_shape(case):
+    import fp8_bf16_causal_amd as fbc
     c = draw(case)
     inp = synth.make_inputs(B=c["B"], S=c["S"], Hq=c["Hq"], Hkv=c["Hkv"], Dqk=c["Dqk"], Dv=128, dtype=c["dtype"],
                             seed=7000 + case, structure=c["structure"], scale=c["scale"])
-    full_check(inp, f"random case {case}: {c}")
+    label = f"random case {case}: {c}"
+    _say(label)
+    dq, dk, dv = inp.descale
+    q, k, v = (t.cuda() for t in (inp.q, inp.k, inp.v))
+    out, lse = fbc.flash_attn_func(q, k, v, inp.scale, causal=True, descale_q=dq, descale_k=dk, descale_v=dv,
+                                   return_lse=True)
+    torch.cuda.synchronize()
+    dt = oracle.BF16 if inp.dtype == "bf16" else oracle.FP8_E4M3
+    ref, ref_lse = oracle.attention(synth.raw_codes(inp.q), synth.raw_codes(inp.k), synth.raw_codes(inp.v), dt,
+                                    inp.scale, dq, dk, dv, return_lse=True)
+    check(inp, out.float().cpu().numpy(), ref, label)
+    le = np.abs(lse.cpu().numpy().astype(np.float64) - ref_lse)
+    tol = lse_tol(inp)
+    worst = int(np.argmax(le - tol))
+    _say(f"{label}: lse max err={le.max():.3e} (tightest row {le.flat[worst]:.3e} <= {tol.flat[worst]:.3e})")
+    assert np.all(le <= tol), label
