@@ -78,6 +78,29 @@ def test_codes_bit_exact_at_extreme_scales(hadamard, exp2):
     assert (ref & 0x7F).min() == 0 and np.sum((ref & 0x7F) < 8) > 1000  # many subnormal codes exercised
 
 
+@pytest.mark.parametrize("case", range(24))
+def test_codes_bit_exact_random(case):
+    """Seeded random tensors: rows 1..5000, dim 64/128/192/256, with or without
+    the rotation, magnitudes 2^e with e drawn in [-60, 40] and a per-row spread
+    of up to 2^+-8, an occasional outlier column and signed zeros: codes bit
+    for bit, s and amax equal."""
+    r = np.random.default_rng(500 + case)
+    rows, dim = int(r.integers(1, 5001)), int(r.choice([64, 128, 192, 256]))
+    had, e = bool(r.integers(0, 2)), int(r.integers(-60, 41))
+    g = torch.Generator().manual_seed(600 + case)
+    x = torch.randn((rows, dim), generator=g) * torch.exp2(torch.randn((rows, 1), generator=g) * 3)
+    if r.integers(0, 2):
+        x[:, int(r.integers(0, dim))] *= 16.0
+    x[int(r.integers(0, rows)), :: 7] = -0.0
+    x = (x * 2.0 ** e).to(torch.bfloat16)
+    _say(f"quantize random case {case}: rows={rows} dim={dim} hadamard={had} 2^{e}")
+    codes, sc = run_quant(x, had)
+    ref, s, amax = quant.quantize_e4m3(bits(x), had)
+    assert sc[1] == amax and sc[0] == s
+    mism = int(np.sum(codes.reshape(ref.shape) != ref))
+    assert mism == 0, f"{mism} codes differ"
+
+
 def test_zero_tensor():
     codes, sc = run_quant(torch.zeros((9, 128), dtype=torch.bfloat16), True)
     assert sc[0] == 1.0 and sc[1] == 0.0 and not codes.any()
